@@ -1,0 +1,125 @@
+"""Planted mistakes in the oracle must be caught by its pins (the pins have teeth).
+
+Each mutation replaces one internal step of `oracle.attention` with a plausible
+wrong version (a dropped term, a wrong sign or index, a transposed operand) and
+requires that at least one pin fails.  Everything runs on the CPU.
+"""
+
+import numpy as np
+import pytest
+
+import oracle_pins as pins
+from oracle import attention as oatt
+
+_orig_rows = oatt._rows_one_head
+_orig_allowed = oatt.allowed
+_orig_probs = oatt._probs_one_head
+
+
+def _rows_no_max_shift_in_lse(q_rows, k, v, rows, scale, causal, bm, mb):
+    o, lse = _orig_rows(q_rows, k, v, rows, scale, causal, bm, mb)
+    cols = oatt._visible_columns(rows, k.shape[0], causal, bm, mb)
+    if cols.size == 0:
+        return o, lse
+    s = np.where(oatt.allowed(rows, k.shape[0], causal, bm, mb, cols=cols), scale * (q_rows @ k[cols].T), -np.inf)
+    m = s.max(axis=1)
+    return o, np.where(np.isfinite(m), lse - m, lse)  # lse without the row maximum
+
+
+def _rows_transposed_k(q_rows, k, v, rows, scale, causal, bm, mb):
+    n = min(k.shape[0], k.shape[1])
+    k2 = k.copy()
+    k2[:n, :n] = k[:n, :n].T
+    return _orig_rows(q_rows, k2, v, rows, scale, causal, bm, mb)
+
+
+def _rows_no_scale(q_rows, k, v, rows, scale, causal, bm, mb):
+    return _orig_rows(q_rows, k, v, rows, 1.0, causal, bm, mb)
+
+
+def _rows_v_off_by_one(q_rows, k, v, rows, scale, causal, bm, mb):
+    return _orig_rows(q_rows, k, np.roll(v, 1, axis=0), rows, scale, causal, bm, mb)
+
+
+def _allowed_strict_causal(rows, n_keys, causal, block_mask=None, mask_block=128, cols=None):
+    ok = _orig_allowed(rows, n_keys, False, block_mask, mask_block, cols)
+    if causal:
+        r = np.asarray(rows)[:, None]
+        c = (np.arange(n_keys) if cols is None else np.asarray(cols))[None, :]
+        ok &= c < r  # j < i instead of j <= i
+    return ok
+
+
+def _allowed_mask_transposed(rows, n_keys, causal, block_mask=None, mask_block=128, cols=None):
+    bm = None if block_mask is None else np.asarray(block_mask).T
+    return _orig_allowed(rows, n_keys, causal, bm, mask_block, cols)
+
+
+def _merge_block_drop_old_l(m_old, l_old, o_old, s_blk, v_blk):
+    """The printed blockwise loop's update: the old normalised output is not re-weighted by the old sum."""
+    m_blk = s_blk.max(axis=1)
+    m_new = np.maximum(m_old, m_blk)
+    seen = np.isfinite(m_new)
+    m0 = np.where(seen, m_new, 0.0)
+    alpha = np.where(np.isfinite(m_old), np.exp(m_old - m0), 0.0)
+    e = np.where(np.isfinite(s_blk), np.exp(s_blk - m0[:, None]), 0.0)
+    l_new = alpha * l_old + e.sum(axis=1)
+    num = alpha[:, None] * o_old + e @ v_blk
+    o_new = np.zeros_like(o_old)
+    o_new[seen] = num[seen] / l_new[seen, None]
+    return m_new, l_new, o_new
+
+
+def _probs_row_sum_off(q, k, ok, scale):
+    p = _orig_probs(q, k, ok, scale)
+    return p * 1.001
+
+
+def _backward_sign_flip(q, k, v, do, scale, causal=False, block_mask=None, mask_block=128, return_delta=False):
+    out = list(_orig_backward(q, k, v, do, scale, causal, block_mask, mask_block, True))
+    out[1] = -out[1]  # dK with the wrong sign
+    return tuple(out) if return_delta else tuple(out[:3])
+
+
+def _backward_delta_dropped(q, k, v, do, scale, causal=False, block_mask=None, mask_block=128, return_delta=False):
+    q64, k64, v64, do64 = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    N = q64.shape[2]
+    ok = oatt.allowed(np.arange(N), N, causal, block_mask, mask_block)
+    dq, dk, dv = np.zeros_like(q64), np.zeros_like(k64), np.zeros_like(v64)
+    D = np.zeros(q64.shape[:3])
+    for b in range(q64.shape[0]):
+        for h in range(q64.shape[1]):
+            P = oatt._probs_one_head(q64[b, h], k64[b, h], ok, scale)
+            dv[b, h] = P.T @ do64[b, h]
+            dS = P * (do64[b, h] @ v64[b, h].T)  # the "- D" term dropped
+            dq[b, h] = scale * dS @ k64[b, h]
+            dk[b, h] = scale * dS.T @ q64[b, h]
+    return (dq, dk, dv, D) if return_delta else (dq, dk, dv)
+
+
+_orig_backward = oatt.backward
+
+MUTATIONS = {
+    "lse_without_max": ("_rows_one_head", _rows_no_max_shift_in_lse, pins.FORWARD_CHECKS),
+    "k_transposed": ("_rows_one_head", _rows_transposed_k, pins.FORWARD_CHECKS),
+    "scale_dropped": ("_rows_one_head", _rows_no_scale, pins.FORWARD_CHECKS),
+    "v_index_shifted": ("_rows_one_head", _rows_v_off_by_one, pins.FORWARD_CHECKS),
+    "causal_strict": ("allowed", _allowed_strict_causal, pins.FORWARD_CHECKS),
+    "block_mask_transposed": ("allowed", _allowed_mask_transposed, pins.FORWARD_CHECKS),
+    "merge_drops_old_l": ("merge_block", _merge_block_drop_old_l, [pins.check_blockwise_equals_one_shot]),
+    "probs_not_normalised": ("_probs_one_head", _probs_row_sum_off, pins.ALL_CHECKS),
+    "dk_sign": ("backward", _backward_sign_flip, pins.BACKWARD_CHECKS),
+    "delta_dropped": ("backward", _backward_delta_dropped, pins.BACKWARD_CHECKS),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn, checks = MUTATIONS[name]
+    monkeypatch.setattr(oatt, attr, fn)
+    import oracle
+
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    bad = pins.failing_checks(checks)
+    assert bad, f"mutation {name} passed every pin"
