@@ -1,0 +1,247 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention hot path on one MI355X.
+
+One step = fa_fwd + fa_bwd (recompute backward) over one batch of the
+long-context causal workload: B=1, H=16, N=16384, d=128, bf16, Q and K drawn as
+1.7 * N(0, 1), V and dO as N(0, 1) (the Path-X length from the FlashAttention
+abstract).  Inputs are resident in HBM before the timed region.
+
+FLOPs are algorithmic: forward 4*B*H*N^2*d, halved under causal masking;
+backward 2.5x the forward (five N x N x d contractions against two).
+Prints one JSON line (metric, value, roofline of the dominant kernel, oracle
+CPU baseline).  Run `python bench.py --help` for options.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 dense bf16 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak, N=512-64K, d=64/128"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_s16k_d128")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the fp64 oracle")
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-workload kernel table")
+    ap.add_argument("--only", choices=["step", "fwd", "bwd"], default="step",
+                    help="time only one direction (for profiling runs)")
+    return ap.parse_args()
+
+
+def flops_fwd(w, density=None):
+    rho = density if density is not None else (0.5 if w.causal else 1.0)
+    return 4.0 * w.B * w.H * w.N * w.N * w.d * rho
+
+
+def sparse_density(mask):
+    import numpy as np
+
+    nb = mask.shape[0]
+    diag = int(np.trace(mask))
+    off = int(mask.sum()) - diag
+    return (off + 0.5 * diag) / float(nb * nb)
+
+
+def to_dev(x, dtype):
+    import torch
+
+    return torch.from_numpy(x).to(dtype).to("cuda:0")
+
+
+def time_calls(fn, n, warmup=2):
+    """Average duration (ms) of fn() measured with HIP events on torch's current stream."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for i in range(n):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / n
+
+
+def kernel_table():
+    """Forward/backward time and TFLOP/s of every bf16 workload (context; not the headline)."""
+    import numpy as np
+    import torch
+
+    from exact_attention_35_amd import api, inputs
+
+    rows = {}
+    for name, w in inputs.WORKLOADS.items():
+        if w.dtype != "bf16":
+            continue
+        q, k, v, _ = inputs.make_qkv(w)
+        tq, tk, tv = to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16)
+        del q, k, v
+        entry = {"shape": list(w.shape), "causal": w.causal}
+        if w.sparse:
+            nb = -(-w.N // inputs.MASK_BLOCK)
+            mask = inputs.make_block_mask(nb, w.density, w.index, causal=w.causal)
+            dens = sparse_density(mask)
+            tm = torch.from_numpy(mask).to("cuda:0")
+            ms = time_calls(lambda: api.forward_blocksparse(tq, tk, tv, tm, w.scale, w.causal), 10)
+            entry.update(fwd_ms=ms, fwd_tflops=flops_fwd(w, dens) / ms / 1e9, density=dens)
+        else:
+            ms = time_calls(lambda: api.forward(tq, tk, tv, w.scale, w.causal), 20)
+            entry.update(fwd_ms=ms, fwd_tflops=flops_fwd(w) / ms / 1e9)
+            if w.backward or w.name == "long_s16k_d128":
+                o, lse = api.forward(tq, tk, tv, w.scale, w.causal)
+                tdo = to_dev(inputs.draw(w.index, inputs.SLOT_DO, w.shape), torch.bfloat16)
+                ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda:0")
+                bms = time_calls(lambda: api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws), 10)
+                entry.update(bwd_ms=bms, bwd_tflops=2.5 * flops_fwd(w) / bms / 1e9)
+        entry["fwd_frac_peak"] = entry["fwd_tflops"] / PEAK_BF16_TFLOPS
+        rows[name] = {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in entry.items()}
+        del tq, tk, tv
+        torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline(w):
+    """The fp64 oracle, as it stands, on head (0, 0) of the workload: forward + backward."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_35_amd import inputs
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    q, k, v, _ = inputs.make_qkv(w, (1, 1, w.N, w.d))
+    do = inputs.draw(w.index, inputs.SLOT_DO, (1, 1, w.N, w.d))
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, w.scale, w.causal)
+    oracle.backward(q, k, v, do, w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    one_head = flops_fwd(w) / (w.B * w.H) * 3.5
+    return {"value": one_head / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"forward + backward of head (0,0) of {w.name} [N={w.N}, d={w.d}, causal] in fp64 NumPy, "
+                      f"{dt:.1f} s; algorithmic flops of that head"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU mode.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from exact_attention_35_amd import api, inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    assert w.dtype == "bf16" and not w.sparse, "the step times a dense bf16 workload"
+    q, k, v, _ = inputs.make_qkv(w)
+    do = inputs.draw(w.index, inputs.SLOT_DO, w.shape)
+    bf = torch.bfloat16
+    tq, tk, tv, tdo = to_dev(q, bf), to_dev(k, bf), to_dev(v, bf), to_dev(do, bf)
+    del q, k, v, do
+    o = torch.empty_like(tq)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+    ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda:0")
+
+    do_fwd = args.only in ("step", "fwd")
+    do_bwd = args.only in ("step", "bwd")
+    if not do_fwd:
+        api.forward(tq, tk, tv, w.scale, w.causal, out=o, lse_out=lse)
+
+    def step(ev=None):
+        if do_fwd:
+            if ev is not None:
+                ev[0].record()
+            api.forward(tq, tk, tv, w.scale, w.causal, out=o, lse_out=lse)
+            if ev is not None:
+                ev[1].record()
+        if do_bwd:
+            if ev is not None:
+                ev[2].record()
+            api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws)
+            if ev is not None:
+                ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    f_fwd = flops_fwd(w)
+    f_bwd = 2.5 * f_fwd
+    f_step = (f_fwd if do_fwd else 0.0) + (f_bwd if do_bwd else 0.0)
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events])) if do_fwd else None
+    bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if do_bwd else None
+    value = f_step * args.steps / elapsed / 1e12
+
+    # dominant kernel by time: the backward's main kernel (fa_bwd also runs two small
+    # memory-bound kernels, well under 2% of its time) or the forward kernel
+    if do_bwd and (not do_fwd or bwd_ms >= fwd_ms):
+        dom, dom_ms, dom_flops = "fa_bwd (bwd_bf16_kernel)", bwd_ms, f_bwd
+    else:
+        dom, dom_ms, dom_flops = "fa_fwd (fwd_bf16_kernel)", fwd_ms, f_fwd
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "launch_ms": round(dom_ms, 4)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "step": {"step": "fa_fwd + fa_bwd", "fwd": "fa_fwd", "bwd": "fa_bwd"}[args.only],
+                   "parallelism": "none (one GPU)"},
+        "fwd": None if fwd_ms is None else {"ms": round(fwd_ms, 4), "tflops": round(f_fwd / fwd_ms / 1e9, 2),
+                                            "frac_peak": round(f_fwd / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
+        "bwd": None if bwd_ms is None else {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / bwd_ms / 1e9, 2),
+                                            "frac_peak": round(f_bwd / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
+        "roofline": roofline,
+    }
+    if not args.no_extra and args.only == "step":
+        del tq, tk, tv, tdo, o, lse, ws
+        torch.cuda.empty_cache()
+        out["workloads"] = kernel_table()
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+// C ABI of libfa.so: argument validation (no HIP call before it passes), then
+// dispatch to the kernel launchers.  Semantics and error codes are documented
+// in include/fa.h.
+#include "fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr long long kMaxGrid = 0x7fffffffLL;
+constexpr size_t kLdsBytes = 160 * 1024;  // gfx950 LDS per workgroup
+constexpr size_t kFwdStaticLds = 2 * 17920 * 2 + 64;  // two K/V stages of the bf16 forward + bookkeeping
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_common(int B, int H, int N, int d, float scale, int causal, int dtype) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (d < 1) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // every grid is at most B*H*ceil(N/64) workgroups and element offsets are 64-bit
+  const long long bh = (long long)B * (long long)H;
+  if (bh > kMaxGrid) return FA_ERR_INVALID_ARG;
+  if (bh * (((long long)N + 63) / 64) > kMaxGrid) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+int fwd_impl(const void* q, const void* k, const void* v, const unsigned char* mask, void* o, float* lse,
+             int B, int H, int N, int d, float scale, int causal, int dtype, void* stream, bool sparse) {
+  int st = check_common(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (sparse && !mask) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return FA_ERR_INVALID_ARG;
+  const size_t n = (size_t)B * H * N;
+  const size_t tb = n * d * elem_bytes(dtype);
+  const Range in[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const Range ro = range_of(o, tb);
+  for (const Range& r : in) {
+    if (overlap(ro, r)) return FA_ERR_INVALID_ARG;
+    if (lse && overlap(range_of(lse, n * 4), r)) return FA_ERR_INVALID_ARG;
+  }
+  if (lse && overlap(range_of(lse, n * 4), ro)) return FA_ERR_INVALID_ARG;
+  if (sparse) {
+    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    const size_t nb = ((size_t)N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+    const size_t list_bytes = nb * (d == 64 ? 1 : 2) * 2 + 16;
+    if (kFwdStaticLds + list_bytes > kLdsBytes) return FA_ERR_UNSUPPORTED;
+    const Range rm = range_of(mask, nb * nb);
+    if (overlap(rm, ro) || (lse && overlap(rm, range_of(lse, n * 4)))) return FA_ERR_INVALID_ARG;
+  }
+  fa::FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.mask = sparse ? mask : nullptr;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.causal = causal;
+  p.dtype = dtype;
+  const hipError_t e = fa::launch_fwd(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK:
+      return "FA_OK: success";
+    case FA_ERR_INVALID_ARG:
+      return "FA_ERR_INVALID_ARG: invalid argument (null or misaligned pointer, bad size, enum or scale, or "
+             "an output overlapping an input)";
+    case FA_ERR_UNSUPPORTED:
+      return "FA_ERR_UNSUPPORTED: unsupported configuration (head dim must be 64 or 128; block-sparse is bf16 "
+             "only; bf16 gradients need bf16 inputs)";
+    case FA_ERR_WORKSPACE:
+      return "FA_ERR_WORKSPACE: workspace missing or smaller than fa_bwd_workspace_size()";
+    case FA_ERR_HIP:
+      return "FA_ERR_HIP: a HIP kernel launch failed";
+    default:
+      return "unknown status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+           float scale, int causal, int dtype, void* stream) {
+  return fwd_impl(q, k, v, nullptr, o, lse, B, H, N, d, scale, causal, dtype, stream, false);
+}
+
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, const unsigned char* block_mask, void* o,
+                       float* lse, int B, int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+  return fwd_impl(q, k, v, block_mask, o, lse, B, H, N, d, scale, causal, dtype, stream, true);
+}
+
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int grad_dtype) {
+  if (check_common(B, H, N, d, 1.0f, 0, grad_dtype) != FA_OK) return 0;
+  const size_t n = (size_t)B * H * N;
+  size_t bytes = (n * 4 + 255) & ~(size_t)255;  // D
+  if (grad_dtype == FA_BF16) bytes += n * d * 4;  // fp32 dQ accumulator
+  return bytes;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+           void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype, int grad_dtype,
+           void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_common(B, H, N, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (grad_dtype != FA_F32 && grad_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (dtype == FA_F32 && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  const size_t need = fa_bwd_workspace_size(B, H, N, d, grad_dtype);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  const size_t n = (size_t)B * H * N;
+  const size_t tb = n * d * elem_bytes(dtype);
+  const size_t gb = n * d * elem_bytes(grad_dtype);
+  const Range ins[6] = {range_of(q, tb), range_of(k, tb), range_of(v, tb),
+                        range_of(o, tb), range_of(lse, n * 4), range_of(dO, tb)};
+  const Range outs[4] = {range_of(dq, gb), range_of(dk, gb), range_of(dv, gb), range_of(workspace, need)};
+  for (int i = 0; i < 4; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
+  }
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dO = dO;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = static_cast<float*>(workspace);
+  const size_t dbytes = (n * 4 + 255) & ~(size_t)255;
+  p.dq_acc = grad_dtype == FA_BF16 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + dbytes)
+                                   : static_cast<float*>(dq);
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.causal = causal;
+  p.dtype = dtype;
+  p.grad_dtype = grad_dtype;
+  const hipError_t e = fa::launch_bwd(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// MFMA operand layouts used throughout (CDNA4, wave64, v_mfma_f32_32x32x16_bf16):
+//   A (32 x 16): lane l supplies row (l % 32), k-slots 8*(l/32) .. 8*(l/32)+7
+//   B (16 x 32): lane l supplies column (l % 32), k-slots 8*(l/32) .. +7
+//   C (32 x 32): lane l holds column (l % 32); accumulator register r holds
+//                row 8*(r/4) + 4*(l/32) + (r%4)
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ uint4 as_uint4(bf16x8 v) { return __builtin_bit_cast(uint4, v); }
+
+__device__ __forceinline__ bf16x8 lds_bf16x8(const unsigned short* p) {
+  return as_bf16x8(*reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Eight fp32 values -> bf16x8, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack_bf16(const f32x16& x, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[base + e];
+  return r;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(unsigned short b) {
+  return __uint_as_float(((unsigned int)b) << 16);
+}
+
+__device__ __forceinline__ unsigned short float_to_bf16_bits(float f) {
+  __bf16 h = (__bf16)f;
+  return __builtin_bit_cast(unsigned short, h);
+}
+
+// Swap bits 2 and 3 of a row index inside its 32-row group.  Rows of an MFMA
+// A-operand tile are stored in LDS in this order so that the accumulator
+// registers 0..7 / 8..15 of lane l hold 8 *consecutive* keys (or queries),
+// 16*(r/8) + 8*(l/32) + (r%8), which is what the next MFMA's k-slots need.
+__device__ __forceinline__ int swap23(int row) {
+  return (row & ~12) | ((row & 4) << 1) | ((row & 8) >> 1);
+}
+
+// Key (or query) offset within a 32-row block held by accumulator register r of
+// an MFMA whose A rows were stored with swap23.
+__device__ __forceinline__ int acc_row_swapped(int r, int half) {
+  return 16 * (r >> 3) + 8 * half + (r & 7);
+}
+
+// Transpose a 4-row x 8-column bf16 micro-block held as four uint4 rows into
+// eight 4-element columns (uint2 each): column e holds rows 0..3 of element e.
+__device__ __forceinline__ uint2 column_of(const uint4 (&rows)[4], int e) {
+  const unsigned int* r0 = reinterpret_cast<const unsigned int*>(&rows[0]);
+  const unsigned int* r1 = reinterpret_cast<const unsigned int*>(&rows[1]);
+  const unsigned int* r2 = reinterpret_cast<const unsigned int*>(&rows[2]);
+  const unsigned int* r3 = reinterpret_cast<const unsigned int*>(&rows[3]);
+  const int w = e >> 1;
+  uint2 out;
+  if (e & 1) {
+    out.x = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
+    out.y = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
+  } else {
+    out.x = (r0[w] & 0xffffu) | (r1[w] << 16);
+    out.y = (r2[w] & 0xffffu) | (r3[w] << 16);
+  }
+  return out;
+}
+
+__device__ __forceinline__ uint4 flip_sign_bf16(uint4 u) {
+  u.x ^= 0x80008000u;
+  u.y ^= 0x80008000u;
+  u.z ^= 0x80008000u;
+  u.w ^= 0x80008000u;
+  return u;
+}
+
+__device__ __forceinline__ uint4 zero_uint4() { return make_uint4(0u, 0u, 0u, 0u); }
+
+}  // namespace fa

@@ -1,0 +1,45 @@
+// Host-side launchers of the attention kernels (internal to libfa.so).
+// Arguments have been validated by the C ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;                 // may be null
+  const unsigned char* mask;  // block-sparse tile mask, null when dense
+  int B, H, N, d;
+  float scale;
+  int causal;
+  int dtype;  // FA_F32 / FA_BF16
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dO;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;   // workspace: [B, H, N] fp32
+  float* dq_acc;  // fp32 [B, H, N, d]: dq itself for fp32 gradients, else workspace
+  int B, H, N, d;
+  float scale;
+  int causal;
+  int dtype;
+  int grad_dtype;
+};
+
+hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,115 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library, libfa.so.
+ *
+ * What is computed.  Exact attention as defined by the everydayai.blog
+ * flash-attention article (opening standard_attention snippet; "The Math Behind
+ * Flash Attention", formula 1) and by the FlashAttention abstract on Tri Dao's
+ * scite.ai author page (IO-aware *exact* attention, tiled so that the N x N
+ * score matrix never reaches HBM; a block-sparse extension).  Per batch b and
+ * head h, with s_ij = scale * <q_i, k_j>:
+ *
+ *     visible(i,j) = (!causal || j <= i) && (no mask || mask[i/128][j/128] != 0)
+ *     O_i   = sum_j softmax_j(s_ij over visible j) v_j
+ *     lse_i = ln sum_{visible j} exp(s_ij)            (natural log, fp32)
+ *
+ * A row with no visible key gets O_i = 0 and lse_i = -inf.
+ *
+ * Conventions shared by every entry point.
+ *   Layout    q, k, v, o, dO, dq, dk, dv: contiguous row-major [B, H, N, d]
+ *             (d innermost); lse and the backward's D: contiguous [B, H, N] fp32.
+ *             All offsets are computed in 64-bit.  Any N >= 1 (ragged tails are
+ *             masked inside the kernels).  d must be 64 or 128.
+ *   dtype     FA_BF16 or FA_F32; it applies to q, k, v, o and dO.  bf16 inputs
+ *             are computed with bf16 MFMA and fp32 accumulation; fp32 inputs with
+ *             fp32 arithmetic throughout.
+ *   Memory    Every pointer is a device pointer owned by the caller and must be
+ *             16-byte aligned.  Outputs must not overlap inputs.  The library
+ *             keeps no state and allocates nothing; the backward takes a
+ *             caller-provided workspace sized by fa_bwd_workspace_size().
+ *   Streams   `stream` is a hipStream_t passed as void* (NULL = default stream).
+ *             Each call validates its arguments on the host, then only enqueues
+ *             kernels on `stream` and returns; buffers must stay valid until the
+ *             stream reaches that point.  Calls are re-entrant and may run
+ *             concurrently on different streams.
+ *   Errors    Every int-returning entry point returns FA_OK (0) or a negative
+ *             code.  Argument validation happens before any HIP call, so an
+ *             invalid call has no effect on the device.  FA_ERR_HIP reports a
+ *             launch error; faults during execution surface at the caller's next
+ *             synchronisation, as with any HIP kernel.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+#define FA_MASK_BLOCK 128 /* rows and keys covered by one block-sparse mask entry */
+
+enum fa_status {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null required pointer, B/H/N < 1, non-finite scale, bad
+                              enum, misaligned pointer, output overlapping an input,
+                              or a size whose grid would not fit */
+  FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}; fp32 with block-sparse; bf16 gradients
+                              for fp32 inputs */
+  FA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than fa_bwd_workspace_size() */
+  FA_ERR_HIP = -4          /* a HIP launch reported an error */
+};
+
+enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 };
+
+/*
+ * Forward.  o <- attention(q, k, v) as defined above; lse <- the row
+ * log-sum-exp (may be NULL when the caller does not need it, e.g. inference).
+ * scale is any finite float (typically 1/sqrt(d)); causal is 0 or 1.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * Block-sparse forward (FlashAttention abstract: extension to block-sparse
+ * attention).  block_mask is a device uint8 array [nb, nb], nb = ceil(N/128),
+ * row-major, shared by every (b, h); key j is visible to query i iff
+ * block_mask[(i/128)*nb + j/128] != 0 and (!causal || j <= i).  Masked
+ * 128x128 tiles cost neither HBM traffic nor MFMA work.  bf16 only.
+ */
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, const unsigned char* block_mask,
+                       void* o, float* lse, int B, int H, int N, int d, float scale, int causal,
+                       int dtype, void* stream);
+
+/*
+ * Bytes of workspace fa_bwd needs: D = rowsum(dO * O) as fp32 [B, H, N], plus an
+ * fp32 [B, H, N, d] dQ accumulator when grad_dtype is FA_BF16.  Returns 0 for
+ * arguments fa_bwd would reject.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int N, int d, int grad_dtype);
+
+/*
+ * Backward.  Gradients of L = sum(dO * O) with respect to q, k and v, for the
+ * same (scale, causal) as the forward that produced o and lse.  The score tiles
+ * are recomputed from lse (everydayai.blog flash-attention article, "Enter Flash
+ * Attention", point 2: recomputation in the backward pass); nothing N x N is
+ * stored.  dq, dk, dv are written in grad_dtype (FA_F32 or FA_BF16; FA_BF16
+ * requires dtype FA_BF16).  The workspace must hold fa_bwd_workspace_size()
+ * bytes; its contents on entry do not matter.  dQ is accumulated with fp32
+ * atomics, so its low bits may differ from run to run.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+           void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+           int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable name of a status code ("unknown status" otherwise). */
+const char* fa_status_string(int status);
+
+/* FA_ABI_VERSION of the loaded library. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

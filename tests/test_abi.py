@@ -1,0 +1,115 @@
+"""The C ABI library loads, exports every declared symbol, and validates before any HIP call (no GPU)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from exact_attention_35_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+INV, UNS, WS = _lib.FA_ERR_INVALID_ARG, _lib.FA_ERR_UNSUPPORTED, _lib.FA_ERR_WORKSPACE
+P = 0x10000  # fake, 16-byte aligned, never dereferenced: validation rejects before using it
+MB = 1 << 32  # spacing that keeps the fake buffers apart
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from exact_attention_35_amd import build
+
+        build.build(verbose=False)
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert names == sorted(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fa_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        s = _lib.status_string(code)
+        assert s.startswith("FA_") and s != "unknown status"
+    assert _lib.status_string(7) == "unknown status"
+
+
+def fwd(lib, q=P, k=P + MB, v=P + 2 * MB, o=P + 3 * MB, lse=P + 4 * MB, B=1, H=1, N=8, d=64,
+        scale=0.125, causal=0, dtype=1):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+def test_fwd_validation(lib):
+    assert fwd(lib, q=None) == INV
+    assert fwd(lib, k=None) == INV
+    assert fwd(lib, v=None) == INV
+    assert fwd(lib, o=None) == INV
+    assert fwd(lib, B=0) == INV
+    assert fwd(lib, H=-1) == INV
+    assert fwd(lib, N=0) == INV
+    assert fwd(lib, d=0) == INV
+    assert fwd(lib, d=32) == UNS
+    assert fwd(lib, d=96) == UNS
+    assert fwd(lib, scale=math.nan) == INV
+    assert fwd(lib, scale=math.inf) == INV
+    assert fwd(lib, causal=2) == INV
+    assert fwd(lib, dtype=5) == INV
+    assert fwd(lib, q=P + 8) == INV  # misaligned
+    assert fwd(lib, lse=P + 4 * MB + 4) == INV
+    assert fwd(lib, o=P) == INV  # output aliases q
+    assert fwd(lib, o=P + 2 * MB + 512) == INV  # output overlaps v
+    assert fwd(lib, lse=P + 3 * MB + 16) == INV  # lse inside o
+    assert fwd(lib, B=1 << 20, H=1 << 12) == INV  # grid would not fit
+
+
+def test_blocksparse_validation(lib):
+    f = lib.fa_fwd_blocksparse
+    base = (P, P + MB, P + 2 * MB)
+    assert f(*base, None, P + 3 * MB, P + 4 * MB, 1, 1, 256, 64, 0.125, 1, 1, None) == INV  # no mask
+    assert f(*base, P + 5 * MB, P + 3 * MB, P + 4 * MB, 1, 1, 256, 64, 0.125, 1, 0, None) == UNS  # fp32
+    assert f(*base, P + 5 * MB, P + 3 * MB, P + 4 * MB, 1, 1, 256, 48, 0.125, 1, 1, None) == UNS
+
+
+def bwd(lib, grad_dtype=0, dtype=1, ws=P + 9 * MB, ws_bytes=None, N=64, d=64, **over):
+    ptrs = dict(q=P, k=P + MB, v=P + 2 * MB, o=P + 3 * MB, lse=P + 4 * MB, do=P + 5 * MB, dq=P + 6 * MB,
+                dk=P + 7 * MB, dv=P + 8 * MB)
+    ptrs.update(over)
+    if ws_bytes is None:
+        ws_bytes = lib.fa_bwd_workspace_size(1, 2, N, d, grad_dtype)
+    return lib.fa_bwd(ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], ptrs["lse"], ptrs["do"], ptrs["dq"], ptrs["dk"],
+                      ptrs["dv"], 1, 2, N, d, 0.125, 1, dtype, grad_dtype, ws, ws_bytes, None)
+
+
+def test_bwd_validation(lib):
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
+        assert bwd(lib, **{name: None}) == INV, name
+    assert bwd(lib, ws=None) == WS
+    assert bwd(lib, ws_bytes=16) == WS
+    assert bwd(lib, grad_dtype=3) == INV
+    assert bwd(lib, dtype=0, grad_dtype=1) == UNS
+    assert bwd(lib, d=80) == UNS
+    assert bwd(lib, dq=P + 4) == INV
+    assert bwd(lib, dk=P + 6 * MB) == INV  # dk aliases dq
+    assert bwd(lib, dv=P + 5 * MB + 64) == INV  # dv overlaps dO
+    assert bwd(lib, ws=P + 7 * MB + 128) == INV  # workspace overlaps dk
+
+
+def test_workspace_size(lib):
+    n = 2 * 3 * 100
+    assert lib.fa_bwd_workspace_size(2, 3, 100, 64, 0) == (n * 4 + 255) // 256 * 256
+    assert lib.fa_bwd_workspace_size(2, 3, 100, 64, 1) == (n * 4 + 255) // 256 * 256 + n * 64 * 4
+    assert lib.fa_bwd_workspace_size(2, 3, 100, 32, 0) == 0
+    assert lib.fa_bwd_workspace_size(0, 3, 100, 64, 0) == 0

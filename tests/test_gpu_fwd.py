@@ -1,0 +1,153 @@
+"""GPU forward parity: the HIP path (through the C ABI) against the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_35_amd import api, inputs
+from gpu_util import TOL_BF16, TOL_F32, TOL_LSE, announce, dev, host, max_err, report
+
+pytestmark = pytest.mark.gpu
+
+BF = torch.bfloat16
+
+
+def run_fwd(q, k, v, dtype, scale, causal):
+    o, lse = api.forward(dev(q, dtype), dev(k, dtype), dev(v, dtype), scale, causal)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+def test_tiny_f32_workload():
+    w = inputs.WORKLOADS["tiny_f32"]
+    announce(w.name)
+    q, k, v, _ = inputs.make_qkv(w)
+    o, lse = run_fwd(q, k, v, torch.float32, w.scale, w.causal)
+    ro, rl = oracle.forward(q, k, v, w.scale, w.causal)
+    eo, el = max_err(o, ro), max_err(lse, rl)
+    report(w.name, o=eo, lse=el)
+    assert eo <= TOL_F32 and el <= TOL_F32
+
+
+def test_bert_large_workload():
+    w = inputs.WORKLOADS["bert_large_s512"]
+    announce(w.name)
+    q, k, v, _ = inputs.make_qkv(w)
+    o, lse = run_fwd(q, k, v, BF, w.scale, w.causal)
+    ro, rl = oracle.forward(q, k, v, w.scale, w.causal)
+    eo, el = max_err(o, ro), max_err(lse, rl)
+    report(w.name, o=eo, lse=el)
+    assert eo <= TOL_BF16 and el <= TOL_LSE
+
+
+def test_long_16k_workload_sampled_rows():
+    w = inputs.WORKLOADS["long_s16k_d128"]
+    announce(w.name)
+    q, k, v, _ = inputs.make_qkv(w)
+    o, lse = run_fwd(q, k, v, BF, w.scale, w.causal)
+    rows = inputs.sample_rows(w.N, w.sample_rows, w.index)
+    ro, rl = oracle.forward_rows(q, k, v, rows, w.scale, w.causal)
+    eo, el = max_err(o[:, :, rows], ro), max_err(lse[:, :, rows], rl)
+    report(w.name, o=eo, lse=el, rows=float(rows.size))
+    assert eo <= TOL_BF16 and el <= TOL_LSE
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+EDGE_N = [1, 2, 17, 64, 127, 128, 129, 300, 1000]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_lengths_bf16(d, causal):
+    for n in EDGE_N:
+        announce(f"fwd bf16 N={n} d={d} causal={causal}")
+        q, k, v, _ = inputs.random_case(1, 2, 3, n, d, "bf16", mult=1.5)
+        scale = api.default_scale(d)
+        o, lse = run_fwd(q, k, v, BF, scale, causal)
+        ro, rl = oracle.forward(q, k, v, scale, causal)
+        eo, el = max_err(o, ro), max_err(lse, rl)
+        report(f"N={n} d={d} causal={causal}", o=eo, lse=el)
+        assert eo <= TOL_BF16 and el <= TOL_LSE, (n, d, causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_lengths_f32(d, causal):
+    for n in (1, 5, 64, 65, 200):
+        announce(f"fwd f32 N={n} d={d} causal={causal}")
+        q, k, v, _ = inputs.random_case(2, 1, 2, n, d, "f32")
+        scale = api.default_scale(d)
+        o, lse = run_fwd(q, k, v, torch.float32, scale, causal)
+        ro, rl = oracle.forward(q, k, v, scale, causal)
+        eo, el = max_err(o, ro), max_err(lse, rl)
+        assert eo <= TOL_F32 and el <= TOL_F32, (n, d, causal, eo, el)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
+def test_scale_values(scale):
+    announce(f"fwd scale={scale}")
+    q, k, v, _ = inputs.random_case(3, 1, 2, 200, 64, "bf16")
+    for causal in (False, True):
+        o, lse = run_fwd(q, k, v, BF, scale, causal)
+        ro, rl = oracle.forward(q, k, v, scale, causal)
+        eo, el = max_err(o, ro), max_err(lse, rl)
+        report(f"scale={scale} causal={causal}", o=eo, lse=el)
+        assert eo <= TOL_BF16 and el <= TOL_LSE
+
+
+def test_large_logits_rescale():
+    """Q, K scaled up so that the running maximum moves many times (stresses the online rescale)."""
+    announce("fwd large logits")
+    q, k, v, _ = inputs.random_case(4, 1, 2, 777, 128, "bf16", mult=4.0)
+    scale = api.default_scale(128)
+    for causal in (False, True):
+        o, lse = run_fwd(q, k, v, BF, scale, causal)
+        ro, rl = oracle.forward(q, k, v, scale, causal)
+        eo, el = max_err(o, ro), max_err(lse, rl)
+        report(f"large logits causal={causal}", o=eo, lse=el)
+        assert eo <= TOL_BF16 and el <= TOL_LSE
+
+
+def test_constant_v_and_ones_column():
+    announce("fwd constant V")
+    q, k, _, _ = inputs.random_case(5, 1, 2, 333, 64, "bf16", mult=2.0)
+    c = inputs.bf16_round(np.linspace(-3, 3, 64).astype(np.float32))
+    v = np.broadcast_to(c, q.shape).copy()
+    for causal in (False, True):
+        o, _ = run_fwd(q, k, v, BF, 0.125, causal)
+        assert max_err(o, np.broadcast_to(c, o.shape)) <= TOL_BF16
+    v2 = inputs.random_case(6, 1, 2, 333, 64, "bf16")[2]
+    v2[..., 7] = 1.0
+    o2, _ = run_fwd(q, k, v2, BF, 0.125, True)
+    assert np.max(np.abs(o2[..., 7] - 1.0)) <= 1e-2
+
+
+def test_deterministic_and_permutation_invariant():
+    announce("fwd determinism")
+    q, k, v, _ = inputs.random_case(7, 2, 2, 520, 128, "bf16")
+    tq, tk, tv = dev(q, BF), dev(k, BF), dev(v, BF)
+    o1, l1 = api.forward(tq, tk, tv, 0.1, True)
+    o2, l2 = api.forward(tq, tk, tv, 0.1, True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    perm = np.random.default_rng(0).permutation(520)
+    o3, l3 = run_fwd(q, k[:, :, perm], v[:, :, perm], BF, 0.1, False)
+    o4, l4 = run_fwd(q, k, v, BF, 0.1, False)
+    assert max_err(o3, o4) <= TOL_BF16 and max_err(l3, l4) <= TOL_LSE
+
+
+def test_no_lse_and_guard_band():
+    """lse may be NULL; outputs are written exactly within their extent."""
+    announce("fwd guard band")
+    B, H, N, d = 1, 2, 130, 64
+    q, k, v, _ = inputs.random_case(8, B, H, N, d, "bf16")
+    n_el = B * H * N * d
+    buf = torch.full((n_el + 2048,), 7.0, dtype=BF, device="cuda:0")
+    out = buf[1024:1024 + n_el].view(B, H, N, d)
+    o, lse = api.forward(dev(q, BF), dev(k, BF), dev(v, BF), 0.125, False, with_lse=False, out=out)
+    torch.cuda.synchronize()
+    assert lse is None
+    assert torch.all(buf[:1024] == 7.0) and torch.all(buf[1024 + n_el:] == 7.0)
+    ro, _ = oracle.forward(q, k, v, 0.125, False)
+    assert max_err(host(out), ro) <= TOL_BF16

@@ -1,0 +1,68 @@
+"""GPU block-sparse forward parity against the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_35_amd import api, inputs
+from gpu_util import TOL_BF16, TOL_LSE, announce, dev, host, max_err, report
+
+pytestmark = pytest.mark.gpu
+
+BF = torch.bfloat16
+
+
+def run_sparse(q, k, v, mask, scale, causal):
+    o, lse = api.forward_blocksparse(dev(q, BF), dev(k, BF), dev(v, BF),
+                                     torch.from_numpy(np.ascontiguousarray(mask)).to("cuda:0"), scale, causal)
+    torch.cuda.synchronize()
+    return host(o), host(lse)
+
+
+def test_blocksparse_64k_workload_sampled_rows():
+    w = inputs.WORKLOADS["blocksparse_s64k"]
+    announce(w.name)
+    q, k, v, _ = inputs.make_qkv(w)
+    nb = w.N // inputs.MASK_BLOCK
+    mask = inputs.make_block_mask(nb, w.density, w.index, causal=w.causal)
+    o, lse = run_sparse(q, k, v, mask, w.scale, w.causal)
+    rows = inputs.sample_rows(w.N, w.sample_rows, w.index)
+    ro, rl = oracle.forward_rows(q, k, v, rows, w.scale, w.causal, mask, inputs.MASK_BLOCK)
+    eo, el = max_err(o[:, :, rows], ro), max_err(lse[:, :, rows], rl)
+    report(w.name, o=eo, lse=el, rows=float(rows.size))
+    assert eo <= TOL_BF16 and el <= TOL_LSE
+    assert np.all(np.isfinite(o))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_random_masks(d, causal):
+    for n in (1, 100, 128, 129, 500, 1030):
+        nb = -(-n // 128)
+        announce(f"sparse N={n} d={d} causal={causal}")
+        q, k, v, _ = inputs.random_case(21, 1, 2, n, d, "bf16", mult=1.5)
+        mask = inputs.random_block_mask(n, nb, 0.4, causal)
+        if nb > 2:
+            mask[1, :] = 0  # a tile row with no visible key: O = 0, lse = -inf
+        scale = api.default_scale(d)
+        o, lse = run_sparse(q, k, v, mask, scale, causal)
+        ro, rl = oracle.forward(q, k, v, scale, causal, mask, inputs.MASK_BLOCK)
+        eo, el = max_err(o, ro), max_err(lse, rl)
+        report(f"sparse N={n} d={d} causal={causal}", o=eo, lse=el)
+        assert eo <= TOL_BF16 and el <= TOL_LSE, (n, d, causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_full_masks_equal_dense(d):
+    """All-ones mask == dense; lower-triangular all-ones mask + causal == causal dense (same kernel arithmetic)."""
+    n = 700
+    nb = -(-n // 128)
+    announce(f"sparse == dense d={d}")
+    q, k, v, _ = inputs.random_case(22, 2, 2, n, d, "bf16")
+    for causal, mask in ((False, np.ones((nb, nb), np.uint8)), (True, np.ones((nb, nb), np.uint8)),
+                         (True, np.tril(np.ones((nb, nb), np.uint8)))):
+        os_, ls_ = run_sparse(q, k, v, mask, 0.1, causal)
+        o, lse = api.forward(dev(q, BF), dev(k, BF), dev(v, BF), 0.1, causal)
+        torch.cuda.synchronize()
+        assert np.array_equal(os_, host(o)) and np.array_equal(ls_, host(lse)), (d, causal)
