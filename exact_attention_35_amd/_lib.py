@@ -41,6 +41,10 @@ def load() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # Bind to the HIP runtime that torch (which owns the memory and streams we are
+    # given) has loaded: loading libfa.so first would pull in a second runtime.
+    import torch  # noqa: F401
+
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
             f"{LIB_PATH} is missing: build it with `python -m exact_attention_35_amd.build` "

@@ -333,11 +333,12 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdKernelArgs a) {
         dk_acc[db] = mfma32(d1, lds_bf16x8(qt + 16), dk_acc[db]);
       }
       // dS (bf16) to LDS, [query][key] with queries in natural order
+      const uint4 u0 = as_uint4(d0), u1 = as_uint4(d1);
 #pragma unroll
-      for (int r = 0; r < 8; ++r) ds_out[acc_row_swapped(r, half) * C::SS] = __builtin_bit_cast(unsigned short, d0[r]);
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-        ds_out[acc_row_swapped(r + 8, half) * C::SS] = __builtin_bit_cast(unsigned short, d1[r]);
+      for (int r = 0; r < 8; ++r) {
+        ds_out[acc_row_swapped(r, half) * C::SS] = bf16_lane_of(u0, r);
+        ds_out[acc_row_swapped(r + 8, half) * C::SS] = bf16_lane_of(u1, r);
+      }
     }
     __syncthreads();  // dS complete; every wave is done with the Q / dO tile
     if (more) bwd_store_qtile<D>(smem, lse2, dlt, tid, regs);
@@ -584,6 +585,7 @@ static void launch_bwd_f32(const BwdParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
+  (void)hipGetLastError();  // clear an error left by an earlier, unrelated HIP call
   const long long rows = (long long)p.B * p.H * p.N;
   if (p.dtype == 0) {
     if (p.d == 64) {

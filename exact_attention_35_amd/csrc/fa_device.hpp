@@ -86,6 +86,12 @@ __device__ __forceinline__ uint2 column_of(const uint4 (&rows)[4], int e) {
   return out;
 }
 
+// Bits of element e (0..7) of eight packed bf16 values.
+__device__ __forceinline__ unsigned short bf16_lane_of(const uint4& u, int e) {
+  const unsigned int w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
+  return (unsigned short)((e & 1) ? (w >> 16) : (w & 0xffffu));
+}
+
 __device__ __forceinline__ uint4 flip_sign_bf16(uint4 u) {
   u.x ^= 0x80008000u;
   u.y ^= 0x80008000u;

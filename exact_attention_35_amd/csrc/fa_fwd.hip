@@ -441,6 +441,8 @@ static hipError_t launch_fwd_f32_t(const FwdParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
+  // an error left by an earlier, unrelated HIP call must not be reported as ours
+  (void)hipGetLastError();
   const bool sparse = p.mask != nullptr;
   if (p.dtype == 0) {  // fp32
     if (p.d == 64) return p.causal ? launch_fwd_f32_t<64, true>(p, stream) : launch_fwd_f32_t<64, false>(p, stream);

@@ -139,12 +139,15 @@ def sample_rows(N: int, count: int, seed_index: int, head: int = 0) -> np.ndarra
 
 def random_case(seed: int, B: int, H: int, N: int, d: int, dtype: str = "bf16", mult: float = 1.0,
                 backward: bool = False):
-    """Small seeded case for edge tests (shapes outside the named workloads)."""
+    """Small seeded case for edge tests (shapes outside the named workloads).
+
+    Q and K are N(0,1) * mult, V (and dO) N(0,1), all rounded to bf16 unless dtype is f32.
+    """
     rng = np.random.default_rng(np.random.SeedSequence([SEED_ROOT, 100, seed, B, H, N, d]))
     out = []
-    for _ in range(4 if backward else 3):
+    for t in range(4 if backward else 3):
         x = rng.standard_normal((B, H, N, d), dtype=np.float32)
-        if mult != 1.0:
+        if mult != 1.0 and t < 2:  # the multiplier scales Q and K only, as in the named workloads
             x = (x * np.float32(mult)).astype(np.float32)
         out.append(bf16_round(x) if dtype == "bf16" else x)
     if not backward:
