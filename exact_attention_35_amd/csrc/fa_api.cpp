@@ -38,6 +38,8 @@ int check_common(int B, int H, int N, int d, float scale, int causal, int dtype)
   const long long bh = (long long)B * (long long)H;
   if (bh > kMaxGrid) return FA_ERR_INVALID_ARG;
   if (bh * (((long long)N + 63) / 64) > kMaxGrid) return FA_ERR_INVALID_ARG;
+  // one head's [N, d] slice is addressed with 32-bit byte offsets
+  if ((long long)N * d * 4 > 0x7fffffffLL) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

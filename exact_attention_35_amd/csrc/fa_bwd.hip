@@ -136,23 +136,26 @@ struct QTileRegs {
 };
 
 template <int D>
-__device__ __forceinline__ void bwd_load_qtile(const BwdKernelArgs& a, size_t hoff, int q0, int tid,
-                                               QTileRegs<D>& t) {
+__device__ __forceinline__ void bwd_load_qtile(const BwdKernelArgs& a, BufRes qres, BufRes dores, size_t hoff,
+                                               int q0, int tid, QTileRegs<D>& t) {
   using C = BwdCfg<D>;
   const int N = a.N;
 #pragma unroll
   for (int j = 0; j < C::MB_PER_THREAD; ++j) {
-    const int mb = tid + j * C::THREADS;  // [0, MB_PER_TENSOR) -> Q, the rest -> dO
+    const int mb = tid + j * C::THREADS;  // [0, MB_PER_TENSOR) -> Q, the rest -> dO (wave-uniform)
     const bool isq = mb < C::MB_PER_TENSOR;
     const int m = isq ? mb : mb - C::MB_PER_TENSOR;
     const int g = m % (C::BM / 4);
     const int c = m / (C::BM / 4);
-    const unsigned short* src = (isq ? a.q : a.dO) + hoff;
+    const BufRes res = isq ? qres : dores;
+    const unsigned int sign = (isq && a.neg) ? 0x80008000u : 0u;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = q0 + 4 * g + r;
-      uint4 u = row < N ? *reinterpret_cast<const uint4*>(src + (size_t)row * D + 8 * c) : zero_uint4();
-      if (isq && a.neg) u = flip_sign_bf16(u);
+      uint4 u = buf_load16(res, (unsigned int)((q0 + 4 * g + r) * D + 8 * c) * 2);  // rows past N: zeros
+      u.x ^= sign;
+      u.y ^= sign;
+      u.z ^= sign;
+      u.w ^= sign;
       t.mb[j][r] = u;
     }
   }
@@ -217,21 +220,22 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdKernelArgs a) {
   const int kt = (int)(blockIdx.x / a.BH);  // causal: small kt = most query tiles, launched first
   const int bh = (int)(blockIdx.x % a.BH);
   const size_t hoff = (size_t)bh * N * D;
+  const unsigned int head_bytes = (unsigned int)N * D * 2;
+  const BufRes qres = make_buf(a.q + hoff, head_bytes);
+  const BufRes kres = make_buf(a.k + hoff, head_bytes);
+  const BufRes vres = make_buf(a.v + hoff, head_bytes);
+  const BufRes dores = make_buf(a.dO + hoff, head_bytes);
   const int k0 = kt * BN;
   const int wave_k0 = k0 + 32 * w;
   const int mykey = wave_k0 + l32;
 
   // K, V rows of this lane's key as MFMA B fragments (d = 16c + 8*half .. +7)
   bf16x8 kf[D / 16], vf[D / 16];
-  {
-    const bool in = mykey < N;
-    const uint4* ks = reinterpret_cast<const uint4*>(a.k + hoff + (size_t)(in ? mykey : 0) * D) + half;
-    const uint4* vs = reinterpret_cast<const uint4*>(a.v + hoff + (size_t)(in ? mykey : 0) * D) + half;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      kf[c] = as_bf16x8(in ? ks[2 * c] : zero_uint4());
-      vf[c] = as_bf16x8(in ? vs[2 * c] : zero_uint4());
-    }
+  for (int c = 0; c < D / 16; ++c) {
+    const unsigned int off = (unsigned int)(mykey * D + 16 * c + 8 * half) * 2;  // keys past N: zeros
+    kf[c] = as_bf16x8(buf_load16(kres, off));
+    vf[c] = as_bf16x8(buf_load16(vres, off));
   }
   // K^T of the workgroup's 128 keys in LDS, for dQ = dS K
   {
@@ -241,10 +245,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdKernelArgs a) {
       const int c = m / (BN / 4);
       uint4 rows[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 4 * g + r;
-        rows[r] = key < N ? *reinterpret_cast<const uint4*>(a.k + hoff + (size_t)key * D + 8 * c) : zero_uint4();
-      }
+      for (int r = 0; r < 4; ++r) rows[r] = buf_load16(kres, (unsigned int)((k0 + 4 * g + r) * D + 8 * c) * 2);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
         *reinterpret_cast<uint2*>(smem + C::OFF_KT + (8 * c + e) * C::KTS + 4 * g) = column_of(rows, e);
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdKernelArgs a) {
 
   QTileRegs<D> regs;
   if (qt_first < nqt) {
-    bwd_load_qtile<D>(a, hoff, qt_first * BM, tid, regs);
+    bwd_load_qtile<D>(a, qres, dores, hoff, qt_first * BM, tid, regs);
     bwd_store_qtile<D>(smem, lse2, dlt, tid, regs);
   }
 
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdKernelArgs a) {
     const int q0 = it * BM;
     const bool more = it + 1 < nqt;
     __syncthreads();  // tile `it` staged; previous dS reads finished
-    if (more) bwd_load_qtile<D>(a, hoff, q0 + BM, tid, regs);
+    if (more) bwd_load_qtile<D>(a, qres, dores, hoff, q0 + BM, tid, regs);
 
 #pragma unroll
     for (int qb = 0; qb < BM / 32; ++qb) {

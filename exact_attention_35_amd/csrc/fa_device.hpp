@@ -102,4 +102,26 @@ __device__ __forceinline__ uint4 flip_sign_bf16(uint4 u) {
 
 __device__ __forceinline__ uint4 zero_uint4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// ---- buffer (V#) memory access: the hardware range check returns zeros for
+// loads past `bytes` and drops stores past it, so tails need no branches.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t BufRes;
+
+__device__ __forceinline__ BufRes make_buf(const void* base, unsigned int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(BufRes r, unsigned int byte_off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void buf_store8(BufRes r, unsigned int byte_off, uint2 x) {
+  u32x2 v;
+  v[0] = x.x;
+  v[1] = x.y;
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 0);
+}
+
 }  // namespace fa

@@ -60,25 +60,21 @@ struct FwdCfg {
   static_assert(K_LOADS * THREADS * 8 == BN * D, "K tile split");
 };
 
+// K and V rows of key tile kt into registers (rows past N read as zeros).
 template <int D, int BN>
-__device__ __forceinline__ void fwd_load_tile(const unsigned short* __restrict__ kh,
-                                              const unsigned short* __restrict__ vh, int kt, int N, int tid,
+__device__ __forceinline__ void fwd_load_tile(BufRes kres, BufRes vres, int kt, int tid,
                                               uint4 (&kreg)[FwdCfg<D, BN>::K_LOADS], uint4 (&vreg)[4]) {
   using C = FwdCfg<D, BN>;
   const int chunk = tid % (D / 8);
   const int row0 = tid / (D / 8);
+  const unsigned int tile_off = (unsigned int)kt * BN * D * 2;
 #pragma unroll
-  for (int p = 0; p < C::K_LOADS; ++p) {
-    const int key = kt * BN + row0 + p * C::K_ROWS_PER_PASS;
-    kreg[p] = key < N ? *reinterpret_cast<const uint4*>(kh + (size_t)key * D + chunk * 8) : zero_uint4();
-  }
+  for (int p = 0; p < C::K_LOADS; ++p)
+    kreg[p] = buf_load16(kres, tile_off + (unsigned int)((row0 + p * C::K_ROWS_PER_PASS) * D + chunk * 8) * 2);
   const int g = tid % (BN / 4);
   const int c = tid / (BN / 4);
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int key = kt * BN + 4 * g + r;
-    vreg[r] = key < N ? *reinterpret_cast<const uint4*>(vh + (size_t)key * D + c * 8) : zero_uint4();
-  }
+  for (int r = 0; r < 4; ++r) vreg[r] = buf_load16(vres, tile_off + (unsigned int)((4 * g + r) * D + c * 8) * 2);
 }
 
 template <int D, int BN>
@@ -131,9 +127,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdKernelArgs a) {
     bh = (int)(blockIdx.x % a.BH);
   }
   const size_t hoff = (size_t)bh * (size_t)N * D;
-  const unsigned short* __restrict__ qh = a.q + hoff;
-  const unsigned short* __restrict__ kh = a.k + hoff;
-  const unsigned short* __restrict__ vh = a.v + hoff;
+  const unsigned int head_bytes = (unsigned int)N * D * 2;
+  const BufRes qres = make_buf(a.q + hoff, head_bytes);
+  const BufRes kres = make_buf(a.k + hoff, head_bytes);
+  const BufRes vres = make_buf(a.v + hoff, head_bytes);
+  const BufRes ores = make_buf(a.o + hoff, head_bytes);
 
   const int q_first = qt * BM;
   const int wave_q0 = q_first + 32 * w;
@@ -173,14 +171,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdKernelArgs a) {
   }
 
   // ---- this lane's query row as MFMA B fragments (d = 16c + 8*half .. +7)
+  // (the sign mask is applied unconditionally so that the loads complete here,
+  // before the tile loop, and never hold up the loop's own prefetches)
   bf16x8 qf[D / 16];
   {
-    const bool in = qrow < N;
-    const uint4* src = reinterpret_cast<const uint4*>(qh + (size_t)(in ? qrow : 0) * D) + half;
+    const unsigned int sign = a.neg ? 0x80008000u : 0u;
 #pragma unroll
     for (int c = 0; c < D / 16; ++c) {
-      uint4 u = in ? src[2 * c] : zero_uint4();
-      if (a.neg) u = flip_sign_bf16(u);
+      uint4 u = buf_load16(qres, (unsigned int)(qrow * D + 16 * c + 8 * half) * 2);
+      u.x ^= sign;
+      u.y ^= sign;
+      u.z ^= sign;
+      u.w ^= sign;
       qf[c] = as_bf16x8(u);
     }
   }
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdKernelArgs a) {
   uint4 vreg[4];
   if (ntiles > 0) {
     const int kt0 = SPARSE ? (int)tile_list[0] : 0;
-    fwd_load_tile<D, BN>(kh, vh, kt0, N, tid, kreg, vreg);
+    fwd_load_tile<D, BN>(kres, vres, kt0, tid, kreg, vreg);
     fwd_store_tile<D, BN>(smem, tid, kreg, vreg);
   }
 
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdKernelArgs a) {
     const bool more = it + 1 < ntiles;
     if (more) {
       const int ktn = SPARSE ? (int)tile_list[it + 1] : it + 1;
-      fwd_load_tile<D, BN>(kh, vh, ktn, N, tid, kreg, vreg);
+      fwd_load_tile<D, BN>(kres, vres, ktn, tid, kreg, vreg);
     }
     __syncthreads();
     const unsigned short* ks = smem + (it & 1) * C::STAGE;
@@ -289,24 +291,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdKernelArgs a) {
   // ---- epilogue
   const float l = l_half + __shfl_xor(l_half, 32);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (qrow < N) {
-    unsigned short* orow = a.o + hoff + (size_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+  for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d0 = 32 * db + 8 * i + 4 * half;
-        uint2 pk;
-        pk.x = (unsigned int)float_to_bf16_bits(oacc[db][4 * i + 0] * inv) |
-               ((unsigned int)float_to_bf16_bits(oacc[db][4 * i + 1] * inv) << 16);
-        pk.y = (unsigned int)float_to_bf16_bits(oacc[db][4 * i + 2] * inv) |
-               ((unsigned int)float_to_bf16_bits(oacc[db][4 * i + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(orow + d0) = pk;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int d0 = 32 * db + 8 * i + 4 * half;
+      uint2 pk;
+      pk.x = (unsigned int)float_to_bf16_bits(oacc[db][4 * i + 0] * inv) |
+             ((unsigned int)float_to_bf16_bits(oacc[db][4 * i + 1] * inv) << 16);
+      pk.y = (unsigned int)float_to_bf16_bits(oacc[db][4 * i + 2] * inv) |
+             ((unsigned int)float_to_bf16_bits(oacc[db][4 * i + 3] * inv) << 16);
+      buf_store8(ores, (unsigned int)(qrow * D + d0) * 2, pk);  // rows past N are dropped
     }
-    if (a.lse != nullptr && half == 0) {
-      a.lse[(size_t)bh * N + qrow] = l > 0.f ? m_run * a.scale_abs + logf(l) : -INFINITY;
-    }
+  }
+  if (a.lse != nullptr && half == 0 && qrow < N) {
+    a.lse[(size_t)bh * N + qrow] = l > 0.f ? m_run * a.scale_abs + logf(l) : -INFINITY;
   }
 }
 
