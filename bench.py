@@ -37,8 +37,9 @@ def parse():
     ap.add_argument("--workload", default="long_s16k_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the fp64 oracle")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-workload kernel table")
-    ap.add_argument("--only", choices=["step", "fwd", "bwd"], default="step",
-                    help="time only one direction (for profiling runs)")
+    ap.add_argument("--only", choices=["step", "fwd", "bwd", "copy"], default="step",
+                    help="time only one direction (for profiling runs); 'copy' times a plain 512 MiB "
+                         "device-to-device copy, the calibration kernel for the HBM byte counters")
     return ap.parse_args()
 
 
@@ -142,6 +143,21 @@ def cpu_baseline(w):
                       f"{dt:.1f} s; algorithmic flops of that head"}
 
 
+COPY_BYTES = 512 << 20
+
+
+def copy_calibration(args):
+    """A plain device copy of COPY_BYTES: its FETCH_SIZE / WRITE_SIZE counters per
+    dispatch, against the known byte count, give the scale of those counters."""
+    import torch
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    ms = time_calls(lambda: dst.copy_(src), args.steps, args.warmup)
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "ms": round(ms, 4),
+                      "GB_per_s": round(2 * COPY_BYTES / ms / 1e6, 1)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -154,6 +170,9 @@ def main():
 
     from exact_attention_35_amd import api, inputs
 
+    if args.only == "copy":
+        copy_calibration(args)
+        return
     w = inputs.WORKLOADS[args.workload]
     assert w.dtype == "bf16" and not w.sparse, "the step times a dense bf16 workload"
     q, k, v, _ = inputs.make_qkv(w)

@@ -86,6 +86,32 @@ __device__ __forceinline__ uint2 column_of(const uint4 (&rows)[4], int e) {
   return out;
 }
 
+// max of three fp32 values in one v_max3_f32 (fmaxf would first canonicalize
+// every input, doubling the instruction count; the scores are never NaN)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+__device__ __forceinline__ float max2f(float a, float b) {
+  float d;
+  asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// Combine a value across the two half-waves (lanes l and l ^ 32) with
+// v_permlane32_swap: each lane ends up holding {own, partner} in the pair.
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return max2f(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Bits of element e (0..7) of eight packed bf16 values.
 __device__ __forceinline__ unsigned short bf16_lane_of(const uint4& u, int e) {
   const unsigned int w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;

@@ -47,72 +47,280 @@ struct FwdKernelArgs {
 
 template <int D, int BN>
 struct FwdCfg {
-  static constexpr int BM = 128;       // queries per workgroup
-  static constexpr int THREADS = 256;  // 4 waves x 32 queries
-  static constexpr int KS = D + 8;     // LDS row stride of K (elements)
-  static constexpr int VS = BN + 8;    // LDS row stride of V^T
-  static constexpr int KTILE = BN * KS;
-  static constexpr int VTILE = D * VS;
-  static constexpr int STAGE = KTILE + VTILE;
-  static constexpr int K_LOADS = BN * D / 8 / THREADS;  // uint4 per thread for K
-  static constexpr int K_ROWS_PER_PASS = THREADS / (D / 8);
-  static_assert((BN / 4) * (D / 8) == THREADS, "one V micro-block per thread");
-  static_assert(K_LOADS * THREADS * 8 == BN * D, "K tile split");
+  static constexpr int BM = 256;            // queries per workgroup (8 waves x 32)
+  static constexpr int NC = D / 8;          // 16-byte chunks per K / V row
+  static constexpr int RPK = 64 / NC;       // rows written by one 1 KB LDS-direct load
+  static constexpr int TILE = BN * D;       // elements of one K (or V) tile in LDS
+  static constexpr int LDS_ELEMS = 6 * TILE;  // K and V, three buffers each
+  static constexpr int NSB = BN / 32;       // 32-key S^T blocks per tile
+  static constexpr int NPT = BN / 16;       // 16-key P fragments per tile
+  static constexpr int NDB = D / 32;        // 32-wide d blocks of the output
+  static constexpr int KB_PER_WAVE = BN * D * 2 / 1024 / 4;  // 1 KB LDS-direct loads per wave per tile
+  static_assert(KB_PER_WAVE * 4 * 1024 == BN * D * 2, "a tile is a whole number of 1 KB loads per wave");
 };
 
-// K and V rows of key tile kt into registers (rows past N read as zeros).
-template <int D, int BN>
-__device__ __forceinline__ void fwd_load_tile(BufRes kres, BufRes vres, int kt, int tid,
-                                              uint4 (&kreg)[FwdCfg<D, BN>::K_LOADS], uint4 (&vreg)[4]) {
-  using C = FwdCfg<D, BN>;
-  const int chunk = tid % (D / 8);
-  const int row0 = tid / (D / 8);
-  const unsigned int tile_off = (unsigned int)kt * BN * D * 2;
-#pragma unroll
-  for (int p = 0; p < C::K_LOADS; ++p)
-    kreg[p] = buf_load16(kres, tile_off + (unsigned int)((row0 + p * C::K_ROWS_PER_PASS) * D + chunk * 8) * 2);
-  const int g = tid % (BN / 4);
-  const int c = tid / (BN / 4);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) vreg[r] = buf_load16(vres, tile_off + (unsigned int)((4 * g + r) * D + c * 8) * 2);
+// ---- LDS tile layouts.  Both tiles are row-major with 16-byte chunks permuted
+// by an XOR of the row ("swizzle") so that the MFMA operand reads hit distinct
+// LDS banks:
+//   K: row R holds key swap23(R) of the tile; chunk c sits at c ^ swz_k(R).
+//      S^T reads: 32 lanes x 16 B of one chunk column over 32 consecutive rows.
+//   V: row R holds key R; chunk c sits at c ^ swz_v(R).  P.V reads use the
+//      transposing LDS read (4 rows x 16 d per 16-lane group).
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// K tile kt -> LDS with 1 KB LDS-direct loads (the four waves of a group
+// cover the tile); rows past N read as zeros.
 template <int D, int BN>
-__device__ __forceinline__ void fwd_store_tile(unsigned short* stage, int tid,
-                                               const uint4 (&kreg)[FwdCfg<D, BN>::K_LOADS],
-                                               const uint4 (&vreg)[4]) {
+__device__ __forceinline__ void dma_k(BufRes kres, unsigned short* kbuf, int kt, int wg, int lane) {
   using C = FwdCfg<D, BN>;
-  unsigned short* ks = stage;
-  unsigned short* vt = stage + C::KTILE;
-  const int chunk = tid % (D / 8);
-  const int row0 = tid / (D / 8);
 #pragma unroll
-  for (int p = 0; p < C::K_LOADS; ++p) {
-    const int row = row0 + p * C::K_ROWS_PER_PASS;
-    *reinterpret_cast<uint4*>(ks + swap23(row) * C::KS + chunk * 8) = kreg[p];
-  }
-  const int g = tid % (BN / 4);
-  const int c = tid / (BN / 4);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    *reinterpret_cast<uint2*>(vt + (c * 8 + e) * C::VS + 4 * g) = column_of(vreg, e);
+  for (int n = 0; n < C::KB_PER_WAVE; ++n) {
+    const int blk = wg * C::KB_PER_WAVE + n;
+    const int row = blk * C::RPK + lane / C::NC;
+    const int c = (lane % C::NC) ^ swz_k<D>(row);
+    const unsigned int off = (unsigned int)((kt * BN + swap23(row)) * D + c * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (lds_void_t*)(kbuf + blk * 512), 16, off, 0, 0, 0);
   }
 }
 
+template <int D, int BN>
+__device__ __forceinline__ void dma_v(BufRes vres, unsigned short* vbuf, int kt, int wg, int lane) {
+  using C = FwdCfg<D, BN>;
+#pragma unroll
+  for (int n = 0; n < C::KB_PER_WAVE; ++n) {
+    const int blk = wg * C::KB_PER_WAVE + n;
+    const int row = blk * C::RPK + lane / C::NC;
+    const int c = (lane % C::NC) ^ swz_v<D>(row);
+    const unsigned int off = (unsigned int)((kt * BN + row) * D + c * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void_t*)(vbuf + blk * 512), 16, off, 0, 0, 0);
+  }
+}
+
+// wait for this wave's LDS-direct loads (they count as vector-memory loads)
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// wait for all but the N most recent vector-memory loads (N < 16)
+template <int N>
+__device__ __forceinline__ void wait_dma_but() { __builtin_amdgcn_s_waitcnt(0x0F70 | N); }
+
+// Per-lane element offsets of the S^T operand reads (one per 16-wide d chunk).
+template <int D>
+struct KOffsets {
+  int off[D / 16];
+};
+template <int D>
+__device__ __forceinline__ KOffsets<D> k_offsets(int l32, int half) {
+  KOffsets<D> k;
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) k.off[cc] = l32 * D + (((2 * cc + half) ^ swz_k<D>(l32)) * 8);
+  return k;
+}
+
+// ---- S^T = K Q^T for one key tile: lane (query l32, half h), register r of block b
+// holds key 32b + 16(r/8) + 8h + (r%8) of the tile (K rows are swap23-ordered in LDS).
+template <int D, int BN>
+__device__ __forceinline__ void qk_tile(const unsigned short* kbuf, const KOffsets<D>& ko, const bf16x8 (&qf)[D / 16],
+                                        f32x16 (&s)[FwdCfg<D, BN>::NSB]) {
+  using C = FwdCfg<D, BN>;
+#pragma unroll
+  for (int b = 0; b < C::NSB; ++b) s[b] = zero16();
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) {
+#pragma unroll
+    for (int b = 0; b < C::NSB; ++b) s[b] = mfma32(lds_bf16x8(kbuf + 32 * b * D + ko.off[cc]), qf[cc], s[b]);
+  }
+}
+
+// Per-lane element offsets of the transposing V reads: base (row part) and one
+// chunk offset per 32-wide d block.
+template <int D>
+struct VOffsets {
+  int base;
+  int blk[D / 32];
+};
+template <int D>
+__device__ __forceinline__ VOffsets<D> v_offsets(int lane) {
+  VOffsets<D> v;
+  const int half = lane >> 5;
+  const int g = lane >> 4;   // 16-lane group: (half, which 16 of the 32 d)
+  const int j = lane & 15;   // source row (j/4) and 4-element column group (j%4)
+  const int dsub = g & 1;
+  const int row = 8 * half + (j >> 2);  // + 16t + 4r at the call
+  v.base = row * D + (j & 1) * 4;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    const int c = 4 * db + 2 * dsub + ((j & 3) >> 1);
+    v.blk[db] = (c ^ swz_v<D>(row)) * 8;
+  }
+  return v;
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+__device__ __forceinline__ uint2 lds_read_tr(const unsigned short* p) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((__attribute__((address_space(3))) unsigned short*)p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// O^T += V^T P^T: lane (query l32, half h), d block db, register r holds d = 32db + 8(r/4) + 4h + r%4.
+// The V^T operand (8 keys 16t + 8h + e for d = 32db + l32) comes from two transposing reads.
+template <int D, int BN>
+__device__ __forceinline__ void pv_tile(const unsigned short* vbuf, const VOffsets<D>& vo, const bf16x8 (&pf)[BN / 16],
+                                        f32x16 (&oacc)[D / 32]) {
+#pragma unroll
+  for (int t = 0; t < BN / 16; ++t) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const unsigned short* p = vbuf + vo.base + vo.blk[db] + 16 * t * D;
+      const uint2 lo = lds_read_tr(p);
+      const uint2 hi = lds_read_tr(p + 4 * D);
+      oacc[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf[t], oacc[db]);
+    }
+  }
+}
+
+// keys past N, and under causal masking keys after the query, get -inf
+template <int BN, bool CAUSAL>
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[BN / 32], int k_first, int qrow, int N, int half) {
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k_first + 32 * b + acc_row_swapped(r, half);
+      const bool hide = key >= N || (CAUSAL && key > qrow);
+      s[b][r] = hide ? -INFINITY : s[b][r];
+    }
+  }
+}
+
+// row maximum of the tile for this lane's query (both half-waves)
+template <int BN>
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[BN / 32]) {
+  float m = max3f(s[0][0], s[0][1], s[0][2]);
+#pragma unroll
+  for (int i = 3; i + 1 < 16 * (BN / 32); i += 2) m = max3f(m, s[i >> 4][i & 15], s[(i + 1) >> 4][(i + 1) & 15]);
+  m = max2f(m, s[BN / 32 - 1][15]);
+  return xhalf_max(m);
+}
+
+// P~ = exp2(S c - m c) -> bf16 MFMA fragments; returns the fp32 row sum of this half-wave
+template <int BN>
+__device__ __forceinline__ float exp_tile(const f32x16 (&s)[BN / 32], float c, float mc, bf16x8 (&pf)[BN / 16]) {
+  float lsum = 0.f;
+#pragma unroll
+  for (int t = 0; t < BN / 16; ++t) {
+    bf16x8 frag;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + e], c, -mc));
+      lsum += p;
+      frag[e] = (__bf16)p;
+    }
+    pf[t] = frag;
+  }
+  return lsum;
+}
+
+// Schedule of one MFMA phase: LDS fragment reads run ahead of the MFMAs
+// (masks: 0x8 MFMA, 0x100 LDS read).  P.V takes two reads per MFMA, S^T one.
+template <int D, int BN>
+__device__ __forceinline__ void sched_gemm_phase() {
+  constexpr int NPV = (BN / 16) * (D / 32);
+  constexpr int NQK = (BN / 32) * (D / 16);
+#pragma unroll
+  for (int i = 0; i < 6; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int i = 0; i < NPV - 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NQK - 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
+// Barrier without a memory fence, for the mid-step switch of the two groups'
+// roles: no LDS hazard crosses it (every buffer reuse is ordered by the
+// end-of-step barrier), and a release fence here would wait for the tile fetch
+// that has just been issued.
+__device__ __forceinline__ void barrier_plain() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// End-of-step barrier of the tile ring: this wave's LDS reads have completed and
+// all but its N most recent LDS-direct loads have landed before it arrives.  The
+// empty asm keeps the compiler from moving memory accesses across; unlike a
+// release fence it does not drain the loads still in flight.
+template <int N>
+__device__ __forceinline__ void barrier_ring() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // lgkmcnt(0), vmcnt(N)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Barrier that orders LDS only: prefetches from global memory stay in flight.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Forward kernel: one workgroup = 256 queries of one (b, h), 8 waves of 32 queries.
+// Waves w and w+4 share a SIMD and form two groups (A = waves 0-3, B = 4-7) that
+// alternate between an MFMA phase G(t) = {O += V(t-1) P(t-1), S(t) = K(t) Q^T} and
+// a VALU phase S(t) = {row max, rescale, P(t) = exp2(S c - m c)}: while one group
+// issues MFMAs the other one's softmax runs on the vector ALU of the same SIMD.
+// The MFMA phase runs at raised wave priority so that its MFMAs issue first.
+// Tiles arrive by LDS-direct loads into a ring of three buffers, two steps
+// ahead of their use (group A fetches V, group B fetches K).
 template <int D, int BN, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdKernelArgs a) {
+__global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   using C = FwdCfg<D, BN>;
   constexpr int BM = C::BM;
-  constexpr int NSB = BN / 32;  // 32-key S^T blocks per tile
-  constexpr int NPT = BN / 16;  // 16-key P fragments per tile
-  constexpr int NDB = D / 32;   // 32-wide d blocks of the output
-  __shared__ __align__(16) unsigned short smem[2 * C::STAGE];
+  constexpr int NSB = C::NSB;
+  constexpr int NPT = C::NPT;
+  constexpr int NDB = C::NDB;
+  // separate arrays (not one): the compiler then knows that LDS reads of one
+  // buffer do not depend on LDS-direct loads still landing in another
+  __shared__ __align__(16) unsigned short kbuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_2[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_2[C::TILE];
   extern __shared__ __align__(16) unsigned short tile_list[];  // SPARSE only
   __shared__ int list_len;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int grp = w >> 2;  // 0: group A, 1: group B
+  const int wg = w & 3;    // wave index inside the group (= SIMD)
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int N = a.N;
@@ -134,21 +342,25 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdKernelArgs a) {
   const BufRes ores = make_buf(a.o + hoff, head_bytes);
 
   const int q_first = qt * BM;
-  const int wave_q0 = q_first + 32 * w;
+  // query blocks interleave between the groups so that causal work is balanced
+  const int wave_q0 = q_first + 32 * (2 * wg + grp);
   const int qrow = wave_q0 + l32;
 
-  // ---- which key tiles this workgroup visits
+  // ---- which key tiles this workgroup visits (a 256-query block spans two mask rows)
   int ntiles;
   if (SPARSE) {
     constexpr int R = 128 / BN;  // key tiles per mask column
-    const unsigned char* mrow = a.mask + (size_t)qt * a.nb;
-    const int ncol = CAUSAL ? min(a.nb, qt + 1) : a.nb;
+    const int r0 = 2 * qt;
+    const int r1 = min(2 * qt + 1, a.nb - 1);
+    const unsigned char* m0 = a.mask + (size_t)r0 * a.nb;
+    const unsigned char* m1 = a.mask + (size_t)r1 * a.nb;
+    const int ncol = CAUSAL ? min(a.nb, r1 + 1) : a.nb;
     const int nkt = (N + BN - 1) / BN;
     if (w == 0) {
       int cnt = 0;
       for (int base = 0; base < ncol; base += 64) {
         const int col = base + lane;
-        const bool on = col < ncol && mrow[col] != 0;
+        const bool on = col < ncol && (m0[col] != 0 || m1[col] != 0);
         const unsigned long long bal = __ballot(on);
         if (on) {
           const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
@@ -169,10 +381,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdKernelArgs a) {
     const int kend = CAUSAL ? min(N, q_first + BM) : N;
     ntiles = (kend + BN - 1) / BN;
   }
+  auto tile_at = [&](int t) __attribute__((always_inline)) -> int {  // steps past the end repeat the last tile
+    const int tt = min(t, ntiles - 1);
+    return SPARSE ? (int)tile_list[tt] : tt;
+  };
+  // this wave's own mask row (block-sparse: the two 128-row halves differ)
+  const unsigned char* my_mrow = SPARSE ? a.mask + (size_t)min(wave_q0 / 128, a.nb - 1) * a.nb : nullptr;
+  auto need_mask = [&](int kt) __attribute__((always_inline)) -> bool {
+    const int k_first = kt * BN;
+    bool m = (k_first + BN > N) || (CAUSAL && k_first + BN - 1 > wave_q0);
+    if (SPARSE) m = m || my_mrow[k_first / 128] == 0;
+    return m;
+  };
 
   // ---- this lane's query row as MFMA B fragments (d = 16c + 8*half .. +7)
-  // (the sign mask is applied unconditionally so that the loads complete here,
-  // before the tile loop, and never hold up the loop's own prefetches)
   bf16x8 qf[D / 16];
   {
     const unsigned int sign = a.neg ? 0x80008000u : 0u;
@@ -186,6 +408,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdKernelArgs a) {
       qf[c] = as_bf16x8(u);
     }
   }
+  const KOffsets<D> ko = k_offsets<D>(l32, half);
+  const VOffsets<D> vo = v_offsets<D>(lane);
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -193,103 +417,110 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdKernelArgs a) {
   float m_run = -INFINITY;
   float l_half = 0.f;
   const float c = a.c;
+  f32x16 s[NSB];
+  bf16x8 pf[NPT];
+#pragma unroll
+  for (int b = 0; b < NSB; ++b) s[b] = zero16();
+#pragma unroll
+  for (int t = 0; t < NPT; ++t) pf[t] = as_bf16x8(zero_uint4());
 
-  uint4 kreg[C::K_LOADS];
-  uint4 vreg[4];
+  // V buffers start as zeros: the first MFMA phase multiplies buffer 2 by P = 0,
+  // and key rows past N (which the range-checked loads may leave unwritten) must
+  // hold finite values, since they are multiplied by P = 0 as well
+  for (int i = tid; i < C::TILE / 8; i += 512) {
+    reinterpret_cast<uint4*>(vbuf_0)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(vbuf_1)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(vbuf_2)[i] = zero_uint4();
+  }
+  barrier_lds();
   if (ntiles > 0) {
-    const int kt0 = SPARSE ? (int)tile_list[0] : 0;
-    fwd_load_tile<D, BN>(kres, vres, kt0, tid, kreg, vreg);
-    fwd_store_tile<D, BN>(smem, tid, kreg, vreg);
-  }
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int kt = SPARSE ? (int)tile_list[it] : it;
-    const bool more = it + 1 < ntiles;
-    if (more) {
-      const int ktn = SPARSE ? (int)tile_list[it + 1] : it + 1;
-      fwd_load_tile<D, BN>(kres, vres, ktn, tid, kreg, vreg);
+    if (grp == 1) {
+      dma_k<D, BN>(kres, kbuf_0, tile_at(0), wg, lane);
+      dma_k<D, BN>(kres, kbuf_1, tile_at(1), wg, lane);
+    } else {
+      dma_v<D, BN>(vres, vbuf_0, tile_at(0), wg, lane);
+      wait_dma();
     }
-    __syncthreads();
-    const unsigned short* ks = smem + (it & 1) * C::STAGE;
-    const unsigned short* vt = ks + C::KTILE;
-    const int k_first = kt * BN;
+  }
+  barrier_ring<C::KB_PER_WAVE>();  // K(1) may still be landing
 
-    // a causal tile entirely after this wave's queries contributes nothing
-    const bool skip = CAUSAL && k_first > wave_q0 + 31;
-    if (!skip) {
-      f32x16 s[NSB];
+  // Branch-free so that the LDS reads run ahead of the MFMAs: at t = 0 the P.V
+  // product uses P = 0 and at t = ntiles the S^T of a stale tile is never used.
+  auto gemm_phase = [&](int t, const unsigned short* kcur, const unsigned short* vprev) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    pv_tile<D, BN>(vprev, vo, pf, oacc);
+    qk_tile<D, BN>(kcur, ko, qf, s);
+    sched_gemm_phase<D, BN>();
+    if (t < ntiles) {
+      const int kt = tile_at(t);
+      if (need_mask(kt)) {
+        mask_tile<BN, CAUSAL>(s, kt * BN, qrow, N, half);
+        if (SPARSE && my_mrow[(kt * BN) / 128] == 0) {
 #pragma unroll
-      for (int b = 0; b < NSB; ++b) {
-        s[b] = zero16();
+          for (int b = 0; b < NSB; ++b)
 #pragma unroll
-        for (int cc = 0; cc < D / 16; ++cc) {
-          const bf16x8 kf = lds_bf16x8(ks + (32 * b + l32) * C::KS + 16 * cc + 8 * half);
-          s[b] = mfma32(kf, qf[cc], s[b]);
-        }
-      }
-      const bool need_mask = (k_first + BN > N) || (CAUSAL && k_first + BN - 1 > wave_q0);
-      if (need_mask) {
-#pragma unroll
-        for (int b = 0; b < NSB; ++b) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k_first + 32 * b + acc_row_swapped(r, half);
-            const bool hide = key >= N || (CAUSAL && key > qrow);
-            s[b][r] = hide ? -INFINITY : s[b][r];
-          }
-        }
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int b = 0; b < NSB; ++b) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[b][r]);
-      }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      // move the basis only when the maximum grows by more than 2^8
-      const bool grow = (mt - m_run) * c > 8.f;
-      float alpha = 1.f;
-      if (grow) {
-        alpha = __builtin_amdgcn_exp2f((m_run - mt) * c);
-        m_run = mt;
-      }
-      if (__ballot(grow)) {
-#pragma unroll
-        for (int i = 0; i < NDB; ++i) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-        }
-      }
-      const float mc = m_run == -INFINITY ? 0.f : m_run * c;
-      float lsum = 0.f;
-#pragma unroll
-      for (int b = 0; b < NSB; ++b) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -mc));
-          s[b][r] = p;
-          lsum += p;
-        }
-      }
-      l_half = l_half * alpha + lsum;
-
-      bf16x8 pf[NPT];
-#pragma unroll
-      for (int t = 0; t < NPT; ++t) pf[t] = pack_bf16(s[t >> 1], 8 * (t & 1));
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-        for (int t = 0; t < NPT; ++t) {
-          const bf16x8 vf = lds_bf16x8(vt + (32 * db + l32) * C::VS + 16 * t + 8 * half);
-          oacc[db] = mfma32(vf, pf[t], oacc[db]);
+            for (int r = 0; r < 16; ++r) s[b][r] = -INFINITY;
         }
       }
     }
-    if (more) fwd_store_tile<D, BN>(smem + ((it + 1) & 1) * C::STAGE, tid, kreg, vreg);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // S(t): softmax statistics and P(t) = exp2(S c - m c)
+  auto softmax_phase = [&]() __attribute__((always_inline)) {
+    const float mt = tile_max<BN>(s);
+    // move the basis only when the maximum grows by more than 2^8 (exact: the
+    // final division uses the same basis)
+    const bool grow = (mt - m_run) * c > 8.f;
+    float alpha = 1.f;
+    if (grow) {
+      alpha = __builtin_amdgcn_exp2f((m_run - mt) * c);
+      m_run = mt;
+    }
+    if (__ballot(grow)) {
+#pragma unroll
+      for (int i = 0; i < NDB; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      }
+    }
+    const float mc = m_run == -INFINITY ? 0.f : m_run * c;
+    l_half = l_half * alpha + exp_tile<BN>(s, c, mc, pf);
+  };
+
+  // Step t.  Buffers rotate with t mod 3: kcur holds K(t), vprev V(t-1); at the
+  // top of phase 2t group A starts fetching V(t+1) into vnext and group B
+  // K(t+2) into knext2 (steps past the end fetch the last tile again, so every
+  // step issues the same number of loads).  At the end of the step each wave
+  // waits for the loads it issued one step earlier, which the next step reads.
+  auto step = [&](int t, const unsigned short* kcur, unsigned short* knext2, const unsigned short* vprev,
+                  unsigned short* vnext) __attribute__((always_inline)) {
+    // phase 2t: A fetches V(t+1) and runs G(t); B fetches K(t+2) and runs S(t-1)
+    if (grp == 0) {
+      dma_v<D, BN>(vres, vnext, tile_at(t + 1), wg, lane);
+      gemm_phase(t, kcur, vprev);
+    } else {
+      dma_k<D, BN>(kres, knext2, tile_at(t + 2), wg, lane);
+      if (t >= 1) softmax_phase();
+    }
+    barrier_plain();
+    // phase 2t+1: A runs S(t); B runs G(t)
+    if (grp == 0) {
+      if (t < ntiles) softmax_phase();
+    } else {
+      gemm_phase(t, kcur, vprev);
+    }
+    barrier_ring<C::KB_PER_WAVE>();
+  };
+  // with no key tile at all (an empty block-sparse row) O = 0 and lse = -inf
+  for (int t = 0; ntiles > 0 && t <= ntiles; t += 3) {
+    step(t, kbuf_0, kbuf_2, vbuf_2, vbuf_1);
+    if (t + 1 <= ntiles) step(t + 1, kbuf_1, kbuf_0, vbuf_0, vbuf_2);
+    if (t + 2 <= ntiles) step(t + 2, kbuf_2, kbuf_1, vbuf_1, vbuf_0);
   }
+  wait_dma();  // no LDS-direct load may outlive the workgroup
 
   // ---- epilogue
-  const float l = l_half + __shfl_xor(l_half, 32);
+  const float l = xhalf_sum(l_half);
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
@@ -415,11 +646,16 @@ static hipError_t launch_fwd_bf16_t(const FwdParams& p, hipStream_t stream) {
   a.scale_abs = sa;
   a.c = fmaxf(sa * kLog2e, 0x1p-100f);
   a.neg = p.scale < 0.f ? 1 : 0;
-  const int nqt = (p.N + 127) / 128;
+  const int nqt = (p.N + 255) / 256;
   const dim3 grid((unsigned)(nqt * a.BH));
   size_t dyn = 0;
   if (SPARSE) dyn = (((size_t)a.nb * (128 / BN) * sizeof(unsigned short)) + 15) & ~(size_t)15;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, CAUSAL, SPARSE>), grid, dim3(256), dyn, stream, a);
+  if (SPARSE && dyn > 0) {
+    // the tile list lives in dynamic LDS next to the static tiles
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, BN, CAUSAL, SPARSE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, CAUSAL, SPARSE>), grid, dim3(512), dyn, stream, a);
   return hipGetLastError();
 }
 

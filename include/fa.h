@@ -17,8 +17,8 @@
  * Conventions shared by every entry point.
  *   Layout    q, k, v, o, dO, dq, dk, dv: contiguous row-major [B, H, N, d]
  *             (d innermost); lse and the backward's D: contiguous [B, H, N] fp32.
- *             All offsets are computed in 64-bit.  Any N >= 1 (ragged tails are
- *             masked inside the kernels).  d must be 64 or 128.
+ *             Any N >= 1 (ragged tails are masked inside the kernels) up to
+ *             N * d * 4 <= 2^31 - 1.  d must be 64 or 128.
  *   dtype     FA_BF16 or FA_F32; it applies to q, k, v, o and dO.  bf16 inputs
  *             are computed with bf16 MFMA and fp32 accumulation; fp32 inputs with
  *             fp32 arithmetic throughout.
@@ -54,8 +54,11 @@ enum fa_status {
   FA_ERR_INVALID_ARG = -1, /* null required pointer, B/H/N < 1, non-finite scale, bad
                               enum, misaligned pointer, output overlapping an input,
                               or a size whose grid would not fit */
-  FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}; fp32 with block-sparse; bf16 gradients
-                              for fp32 inputs */
+  FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}; N * d * 4 > 2^31 - 1 (one head's slice is
+                              addressed with 32-bit byte offsets); fp32 with block-sparse;
+                              a block-sparse N whose tile list does not fit in LDS
+                              (N above about 4.19M at d = 64, 2.09M at d = 128); bf16 gradients for
+                              fp32 inputs */
   FA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than fa_bwd_workspace_size() */
   FA_ERR_HIP = -4          /* a HIP launch reported an error */
 };

@@ -81,6 +81,16 @@ def test_blocksparse_validation(lib):
     assert f(*base, None, P + 3 * MB, P + 4 * MB, 1, 1, 256, 64, 0.125, 1, 1, None) == INV  # no mask
     assert f(*base, P + 5 * MB, P + 3 * MB, P + 4 * MB, 1, 1, 256, 64, 0.125, 1, 0, None) == UNS  # fp32
     assert f(*base, P + 5 * MB, P + 3 * MB, P + 4 * MB, 1, 1, 256, 48, 0.125, 1, 1, None) == UNS
+    # the visited-tile list of a 256-query block must fit in LDS next to the K/V tiles
+    for d, n_bad in ((64, 4190208 + 128), (128, 2095104 + 128)):
+        assert f(*base, P + 5 * MB, P + 3 * MB, P + 4 * MB, 1, 1, n_bad, d, 0.125, 1, 1, None) == UNS
+
+
+def test_head_slice_limit(lib):
+    # one head's [N, d] slice is addressed with 32-bit byte offsets
+    ptrs = (P, P + MB, P + 2 * MB, P + 3 * MB, P + 4 * MB)
+    assert lib.fa_fwd(*ptrs, 1, 1, (1 << 31) // 256 + 1, 64, 0.125, 1, 1, None) == UNS
+    assert lib.fa_fwd(*ptrs, 1, 1, (1 << 31) // 512 + 1, 128, 0.125, 1, 1, None) == UNS
 
 
 def bwd(lib, grad_dtype=0, dtype=1, ws=P + 9 * MB, ws_bytes=None, N=64, d=64, **over):
