@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--workload", default="long_s16k_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the fp64 oracle")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-workload kernel table")
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="print a text summary of the rocprofv3 CSV output under DIR and exit")
     ap.add_argument("--only", choices=["step", "fwd", "bwd", "copy"], default="step",
                     help="time only one direction (for profiling runs); 'copy' times a plain 512 MiB "
                          "device-to-device copy, the calibration kernel for the HBM byte counters")
@@ -145,6 +147,62 @@ def cpu_baseline(w):
 
 COPY_BYTES = 512 << 20
 
+# HBM traffic per launch of the two main kernels on long_s16k_d128, from separate
+# rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs (KiB per dispatch), each
+# scaled by what the same counter reads for the COPY_BYTES calibration copy
+# (FETCH_SIZE reads half of the copied bytes, WRITE_SIZE all of them).  A figure
+# holds only for the sources it was taken on: when their hash differs the
+# traffic is reported as null.
+TRAFFIC_FETCH_SCALE = 2.0
+TRAFFIC_WRITE_SCALE = 1.0
+MEASURED_TRAFFIC = {
+    "fwd": {"fetch_kib": 230209.0, "write_kib": 66561.0,
+            "sources": ["fa_fwd.hip", "fa_device.hpp"], "sha256": "d85d67142828bec5a73fe7f918ae3e2ebf514752111f88dfbf6bfff0cc5dad8d"},
+    "bwd": {"fetch_kib": 366939.0, "write_kib": 8716288.0,
+            "sources": ["fa_bwd.hip", "fa_device.hpp"], "sha256": "1671a277069fc28af9c91fb1f9d864e1e6583827c88f28fa7f05d55be0e999f7"},
+}
+
+
+def sources_sha256(names):
+    import hashlib
+
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_attention_35_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(which):
+    """HBM bytes per launch of the forward or backward kernel, or None when stale."""
+    m = MEASURED_TRAFFIC[which]
+    if sources_sha256(m["sources"]) != m["sha256"]:
+        return None
+    return m["fetch_kib"] * 1024 * TRAFFIC_FETCH_SCALE + m["write_kib"] * 1024 * TRAFFIC_WRITE_SCALE
+
+
+def profile_summary(d):
+    """Text summary of a rocprofv3 output tree: kernel-trace stats and PMC byte counters."""
+    import csv
+    import glob
+    from collections import defaultdict
+
+    lines = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
+        lines.append(f"kernel-trace stats ({os.path.relpath(f, d)}):")
+        lines.append(f"  {'calls':>5} {'avg us':>10} {'min us':>10} {'max us':>10} {'%':>6}  kernel")
+        for r in csv.DictReader(open(f)):
+            lines.append(f"  {r['Calls']:>5} {float(r['AverageNs']) / 1e3:10.1f} {float(r['MinNs']) / 1e3:10.1f} "
+                         f"{float(r['MaxNs']) / 1e3:10.1f} {float(r['Percentage']):6.2f}  {r['Name'][:90]}")
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        agg = defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            agg[(r["Counter_Name"], r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        lines.append(f"pmc ({os.path.relpath(f, d)}):")
+        for (c, k), v in agg.items():
+            lines.append(f"  {c:>10} {len(v):3d} dispatches, mean {sum(v) / len(v):12.1f} KiB  {k[:90]}")
+    return "\n".join(lines)
+
 
 def copy_calibration(args):
     """A plain device copy of COPY_BYTES: its FETCH_SIZE / WRITE_SIZE counters per
@@ -160,6 +218,9 @@ def copy_calibration(args):
 
 def main():
     args = parse()
+    if args.profile_summary:
+        print(profile_summary(args.profile_summary))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU mode.",
               file=sys.stderr)
@@ -224,12 +285,14 @@ def main():
     # dominant kernel by time: the backward's main kernel (fa_bwd also runs two small
     # memory-bound kernels, well under 2% of its time) or the forward kernel
     if do_bwd and (not do_fwd or bwd_ms >= fwd_ms):
-        dom, dom_ms, dom_flops = "fa_bwd (bwd_bf16_kernel)", bwd_ms, f_bwd
+        dom, dom_ms, dom_flops, which = "fa_bwd (bwd_bf16_kernel)", bwd_ms, f_bwd, "bwd"
     else:
-        dom, dom_ms, dom_flops = "fa_fwd (fwd_bf16_kernel)", fwd_ms, f_fwd
+        dom, dom_ms, dom_flops, which = "fa_fwd (fwd_bf16_kernel)", fwd_ms, f_fwd, "fwd"
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic = measured_traffic(which) if w.name == "long_s16k_d128" else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if traffic is None else round(traffic), "kernel": dom,
                 "launch_ms": round(dom_ms, 4)}
 
     out = {
