@@ -130,9 +130,7 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, const unsign
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int grad_dtype) {
   if (check_common(B, H, N, d, 1.0f, 0, grad_dtype) != FA_OK) return 0;
   const size_t n = (size_t)B * H * N;
-  size_t bytes = (n * 4 + 255) & ~(size_t)255;  // D
-  if (grad_dtype == FA_BF16) bytes += n * d * 4;  // fp32 dQ accumulator
-  return bytes;
+  return n * 8;  // per row: (lse * log2 e, D), two fp32
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
@@ -171,10 +169,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.delta = static_cast<float*>(workspace);
-  const size_t dbytes = (n * 4 + 255) & ~(size_t)255;
-  p.dq_acc = grad_dtype == FA_BF16 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + dbytes)
-                                   : static_cast<float*>(dq);
+  p.stats = static_cast<float*>(workspace);
   p.B = B;
   p.H = H;
   p.N = N;

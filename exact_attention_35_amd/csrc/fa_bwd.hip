@@ -9,28 +9,32 @@
 //   dV  = P^T dO    dP = dO V^T    dS = P * (dP - D)
 //   dQ  = scale dS K              dK = scale dS^T Q
 //
-// bf16 kernel: one workgroup owns 128 keys of one (b, h) (4 waves x 32 keys);
-// its K and V rows stay in VGPRs (MFMA B operands) and dK, dV accumulate in
-// registers.  It walks the query tiles (64 rows; under causal masking only
-// those at or after its keys), staging Q and dO through LDS both row-major and
-// transposed.  Per wave and 32-query block: S = Q K^T and dP = dO V^T on MFMA
-// (one key per lane), P = exp2(S c - lse log2 e), dS = P (dP - D), then
-// dV += P^T dO and dK += dS^T Q from the registers.  dS goes through LDS so
-// that the workgroup computes dQ_i = dS K over all its 128 keys and adds it to
-// an fp32 accumulator with atomics.
+// bf16 path, three kernels:
+//   * bwd_prep_kernel: per row, D and lse log2(e) (+inf for a row with no
+//     visible key, so that its P is 0), stored as one float2;
+//   * bwd_dkdv_kernel: one workgroup owns 128 keys; it streams 64-query tiles
+//     of Q and dO through LDS and accumulates dK, dV in registers;
+//   * bwd_dq_kernel: one workgroup owns 256 queries; it streams K and V tiles
+//     through LDS and accumulates dQ in registers.
+// Each gradient is owned by exactly one workgroup, so there are no atomics
+// and the results are deterministic; the price is that S and dP are
+// recomputed by both the dK/dV and the dQ kernel (seven tile contractions per
+// (query, key) tile pair instead of five).
 #include <math.h>
 
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
+#include "fa_tiles.hpp"
 
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O), fp32 out.  T = unsigned short (bf16 bits) or float.
+// stats[row] = (lse * log2 e, D = rowsum(dO * O)).  T = unsigned short (bf16 bits) or float.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o, const T* __restrict__ dO,
-                                                        float* __restrict__ delta, long long rows) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, const T* __restrict__ dO,
+                                                       const float* __restrict__ lse, float2* __restrict__ stats,
+                                                       long long rows) {
   constexpr int EPT = 16 / sizeof(T);  // elements per 16-byte load
   constexpr int TPR = D / EPT;         // threads per row
   constexpr int RPB = 256 / TPR;       // rows per block
@@ -55,334 +59,484 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const T* __restrict__ o,
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && part == 0) delta[row] = acc;
-}
-
-__global__ __launch_bounds__(256) void fill_zero_kernel(float4* __restrict__ p, long long n4) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i < n4) p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
-__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float4* __restrict__ src,
-                                                          uint2* __restrict__ dst, long long n4) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i < n4) {
-    const float4 x = src[i];
-    uint2 r;
-    r.x = (unsigned int)float_to_bf16_bits(x.x) | ((unsigned int)float_to_bf16_bits(x.y) << 16);
-    r.y = (unsigned int)float_to_bf16_bits(x.z) | ((unsigned int)float_to_bf16_bits(x.w) << 16);
-    dst[i] = r;
+  if (row < rows && part == 0) {
+    const float l = lse[row];
+    stats[row] = make_float2(l == -INFINITY ? INFINITY : l * kLog2e, acc);
   }
 }
 
-// ---------------------------------------------------------------------------
-// bf16 main backward kernel
-// ---------------------------------------------------------------------------
-struct BwdKernelArgs {
+__device__ __forceinline__ void buf_store16f(BufRes r, unsigned int byte_off, float a0, float a1, float a2, float a3) {
+  u32x4 v;
+  v[0] = __float_as_uint(a0);
+  v[1] = __float_as_uint(a1);
+  v[2] = __float_as_uint(a2);
+  v[3] = __float_as_uint(a3);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 0);
+}
+
+// Store a [rows x D] gradient block held as MFMA accumulators with lane = row
+// (row index `row`, half h) and register r of d block db at d = 32db + 8(r/4) + 4h + r%4,
+// times `mul`, as fp32 or bf16.  Rows past the head are dropped by the range check.
+template <int D>
+__device__ __forceinline__ void store_grad_rows(void* base, size_t hoff, int N, int row, int half, int grad_bf16,
+                                                const f32x16 (&acc)[D / 32], float mul) {
+  if (grad_bf16) {
+    const BufRes res = make_buf(static_cast<unsigned short*>(base) + hoff, (unsigned int)N * D * 2);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * db + 8 * i + 4 * half;
+        uint2 pk;
+        pk.x = (unsigned int)float_to_bf16_bits(acc[db][4 * i + 0] * mul) |
+               ((unsigned int)float_to_bf16_bits(acc[db][4 * i + 1] * mul) << 16);
+        pk.y = (unsigned int)float_to_bf16_bits(acc[db][4 * i + 2] * mul) |
+               ((unsigned int)float_to_bf16_bits(acc[db][4 * i + 3] * mul) << 16);
+        buf_store8(res, (unsigned int)(row * D + d0) * 2, pk);
+      }
+    }
+  } else {
+    const BufRes res = make_buf(static_cast<float*>(base) + hoff, (unsigned int)N * D * 4);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d0 = 32 * db + 8 * i + 4 * half;
+        buf_store16f(res, (unsigned int)(row * D + d0) * 4, acc[db][4 * i + 0] * mul, acc[db][4 * i + 1] * mul,
+                     acc[db][4 * i + 2] * mul, acc[db][4 * i + 3] * mul);
+      }
+    }
+  }
+}
+
+struct BwdBf16Args {
   const unsigned short* q;
   const unsigned short* k;
   const unsigned short* v;
   const unsigned short* dO;
-  const float* lse;
-  const float* delta;
-  float* dq_acc;
+  const float2* stats;  // per row: (lse log2 e, D)
+  void* dq;
   void* dk;
   void* dv;
   int grad_bf16;
   int BH;
   int N;
-  float c;          // |scale| * log2(e), clamped away from 0
-  float scale_abs;  // factor of dK (Q is negated when scale < 0)
-  float scale;      // factor of dQ
-  int neg;
+  float c;      // |scale| * log2(e), clamped away from 0
+  float scale;  // factor of dQ and dK
+  int neg;      // scale < 0: the sign of Q (dQ kernel) or K (dK/dV kernel) is flipped on load
 };
 
-template <int D>
-struct BwdCfg {
-  static constexpr int BN = 128;  // keys per workgroup
-  static constexpr int BM = 64;   // queries per step
-  static constexpr int THREADS = 256;
-  static constexpr int RS = D + 8;    // row-major Q / dO stride
-  static constexpr int TS = BM + 8;   // transposed Q / dO stride
-  static constexpr int KTS = BN + 8;  // transposed K stride
-  static constexpr int SS = BN + 8;   // dS stride
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_DO = OFF_Q + BM * RS;
-  static constexpr int OFF_QT = OFF_DO + BM * RS;
-  static constexpr int OFF_DOT = OFF_QT + D * TS;
-  static constexpr int OFF_KT = OFF_DOT + D * TS;
-  static constexpr int OFF_DS = OFF_KT + D * KTS;
-  static constexpr int ELEMS = OFF_DS + BM * SS;  // unsigned short elements
-  static constexpr int MB_PER_TENSOR = (BM / 4) * (D / 8);  // 4x8 micro-blocks per Q (or dO) tile
-  static constexpr int MB_PER_THREAD = 2 * MB_PER_TENSOR / THREADS;  // Q and dO together
-  static_assert(MB_PER_THREAD * THREADS == 2 * MB_PER_TENSOR, "micro-block split");
-};
-
-// Stage one 4-row x 8-column micro-block both row-major (rows stored with
-// swap23 inside 32-row groups) and transposed.
-template <int RS, int TS>
-__device__ __forceinline__ void stage_micro_block(unsigned short* rowmajor, unsigned short* transposed,
-                                                  const uint4 (&rows)[4], int g, int c) {
+// ---------------------------------------------------------------------------
+// dQ kernel: one workgroup = 256 queries of one (b, h), 8 waves of 32 queries,
+// organised like the forward: waves w and w+4 share a SIMD and form groups A
+// (waves 0-3) and B (4-7) that alternate an MFMA phase and a vector phase.
+//   G(t): dQ^T += K(t-1)^T dS^T(t-1);  S^T(t) = K(t) Q^T;  dP^T(t) = V(t) dO^T
+//   E(t): P = exp2(S c - lse log2 e) (0 where masked);  dS = P (dP - D)
+// One query per lane: its lse and D are one register each.  K and V tiles
+// (both in the K layout) arrive by LDS-direct loads into rings of three
+// buffers: K one step ahead (group B), V two steps ahead (group A).
+// ---------------------------------------------------------------------------
+template <int D, int BN>
+__device__ __forceinline__ void sched_dq_gemm() {
+  constexpr int NKT = (BN / 16) * (D / 32);      // dQ MFMAs, two transposing reads each
+  constexpr int NQK = 2 * (BN / 32) * (D / 16);  // S^T and dP^T MFMAs, one read each
 #pragma unroll
-  for (int r = 0; r < 4; ++r) *reinterpret_cast<uint4*>(rowmajor + swap23(4 * g + r) * RS + 8 * c) = rows[r];
+  for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) *reinterpret_cast<uint2*>(transposed + (8 * c + e) * TS + 4 * g) = column_of(rows, e);
+  for (int i = 0; i < NKT - 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NQK - 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
-template <int D>
-struct QTileRegs {
-  uint4 mb[BwdCfg<D>::MB_PER_THREAD][4];
-  float stat;
-};
-
-template <int D>
-__device__ __forceinline__ void bwd_load_qtile(const BwdKernelArgs& a, BufRes qres, BufRes dores, size_t hoff,
-                                               int q0, int tid, QTileRegs<D>& t) {
-  using C = BwdCfg<D>;
-  const int N = a.N;
-#pragma unroll
-  for (int j = 0; j < C::MB_PER_THREAD; ++j) {
-    const int mb = tid + j * C::THREADS;  // [0, MB_PER_TENSOR) -> Q, the rest -> dO (wave-uniform)
-    const bool isq = mb < C::MB_PER_TENSOR;
-    const int m = isq ? mb : mb - C::MB_PER_TENSOR;
-    const int g = m % (C::BM / 4);
-    const int c = m / (C::BM / 4);
-    const BufRes res = isq ? qres : dores;
-    const unsigned int sign = (isq && a.neg) ? 0x80008000u : 0u;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      uint4 u = buf_load16(res, (unsigned int)((q0 + 4 * g + r) * D + 8 * c) * 2);  // rows past N: zeros
-      u.x ^= sign;
-      u.y ^= sign;
-      u.z ^= sign;
-      u.w ^= sign;
-      t.mb[j][r] = u;
-    }
-  }
-  t.stat = 0.f;
-  if (tid < 2 * C::BM) {
-    const int i = tid % C::BM;
-    const int row = q0 + i;
-    const size_t idx = hoff / D + (size_t)row;
-    if (tid < C::BM) {
-      // P = exp2(S c - lse log2 e); a row past N or with no visible key gets +inf so that P = 0
-      float x = INFINITY;
-      if (row < N) {
-        const float l = a.lse[idx];
-        x = l == -INFINITY ? INFINITY : l * kLog2e;
-      }
-      t.stat = x;
-    } else {
-      t.stat = row < N ? a.delta[idx] : 0.f;
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void bwd_store_qtile(unsigned short* smem, float* lse2, float* dlt, int tid,
-                                                const QTileRegs<D>& t) {
-  using C = BwdCfg<D>;
-#pragma unroll
-  for (int j = 0; j < C::MB_PER_THREAD; ++j) {
-    const int mb = tid + j * C::THREADS;
-    const bool isq = mb < C::MB_PER_TENSOR;
-    const int m = isq ? mb : mb - C::MB_PER_TENSOR;
-    const int g = m % (C::BM / 4);
-    const int c = m / (C::BM / 4);
-    stage_micro_block<C::RS, C::TS>(smem + (isq ? C::OFF_Q : C::OFF_DO), smem + (isq ? C::OFF_QT : C::OFF_DOT),
-                                    t.mb[j], g, c);
-  }
-  if (tid < C::BM) {
-    lse2[tid] = t.stat;
-  } else if (tid < 2 * C::BM) {
-    dlt[tid - C::BM] = t.stat;
-  }
-}
-
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(BwdKernelArgs a) {
-  using C = BwdCfg<D>;
-  constexpr int BN = C::BN;
-  constexpr int BM = C::BM;
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
+  using C = TileCfg<D, BN>;
+  constexpr int BM = 256;
+  constexpr int NSB = C::NSB;
+  constexpr int NPT = C::NPT;
   constexpr int NDB = D / 32;
-  __shared__ __align__(16) unsigned short smem[C::ELEMS];
-  __shared__ __align__(16) float lse2[BM];
-  __shared__ __align__(16) float dlt[BM];
+  __shared__ __align__(16) unsigned short kbuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_2[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_2[C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
+  const int grp = w >> 2;
+  const int wg = w & 3;
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int N = a.N;
-  const int nkt = (N + BN - 1) / BN;
-  (void)nkt;
-  const int kt = (int)(blockIdx.x / a.BH);  // causal: small kt = most query tiles, launched first
+  const int nqt = (N + BM - 1) / BM;
+  const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / a.BH) : (int)(blockIdx.x / a.BH);  // longest rows first
   const int bh = (int)(blockIdx.x % a.BH);
-  const size_t hoff = (size_t)bh * N * D;
+  const size_t hoff = (size_t)bh * (size_t)N * D;
   const unsigned int head_bytes = (unsigned int)N * D * 2;
   const BufRes qres = make_buf(a.q + hoff, head_bytes);
   const BufRes kres = make_buf(a.k + hoff, head_bytes);
   const BufRes vres = make_buf(a.v + hoff, head_bytes);
   const BufRes dores = make_buf(a.dO + hoff, head_bytes);
-  const int k0 = kt * BN;
-  const int wave_k0 = k0 + 32 * w;
-  const int mykey = wave_k0 + l32;
 
-  // K, V rows of this lane's key as MFMA B fragments (d = 16c + 8*half .. +7)
-  bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    const unsigned int off = (unsigned int)(mykey * D + 16 * c + 8 * half) * 2;  // keys past N: zeros
-    kf[c] = as_bf16x8(buf_load16(kres, off));
-    vf[c] = as_bf16x8(buf_load16(vres, off));
+  const int q_first = qt * BM;
+  const int wave_q0 = q_first + 32 * (2 * wg + grp);
+  const int qrow = wave_q0 + l32;
+  const int kend = CAUSAL ? min(N, q_first + BM) : N;
+  const int ntiles = (kend + BN - 1) / BN;
+  auto tile_at = [&](int t) __attribute__((always_inline)) -> int { return min(t, ntiles - 1); };
+  auto need_mask = [&](int kt) __attribute__((always_inline)) -> bool {
+    const int k_first = kt * BN;
+    return (k_first + BN > N) || (CAUSAL && k_first + BN - 1 > wave_q0);
+  };
+
+  // Every tile buffer starts as zeros: K(-1) is read (times dS = 0) by the first
+  // MFMA phase, and rows past N (which the range-checked loads may leave
+  // unwritten) are multiplied by zeros, so they must hold finite values.
+  for (int i = tid; i < C::TILE / 8; i += 512) {
+    reinterpret_cast<uint4*>(kbuf_0)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(kbuf_1)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(kbuf_2)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(vbuf_0)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(vbuf_1)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(vbuf_2)[i] = zero_uint4();
   }
-  // K^T of the workgroup's 128 keys in LDS, for dQ = dS K
+  barrier_lds();
+  if (grp == 1) {
+    dma_k<D, BN>(kres, kbuf_0, tile_at(0), wg, lane);
+    wait_dma();
+  } else {
+    dma_k<D, BN>(vres, vbuf_0, tile_at(0), wg, lane);
+    dma_k<D, BN>(vres, vbuf_1, tile_at(1), wg, lane);
+  }
+  barrier_ring<C::KB_PER_WAVE>();  // V(1) may still be landing
+
+  // ---- this lane's query: Q and dO rows as MFMA B fragments, lse and D
+  bf16x8 qf[D / 16], dof[D / 16];
   {
-    constexpr int MBK = (BN / 4) * (D / 8);
-    for (int m = tid; m < MBK; m += C::THREADS) {
-      const int g = m % (BN / 4);
-      const int c = m / (BN / 4);
-      uint4 rows[4];
+    const unsigned int sign = a.neg ? 0x80008000u : 0u;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rows[r] = buf_load16(kres, (unsigned int)((k0 + 4 * g + r) * D + 8 * c) * 2);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint2*>(smem + C::OFF_KT + (8 * c + e) * C::KTS + 4 * g) = column_of(rows, e);
+    for (int c = 0; c < D / 16; ++c) {
+      const unsigned int off = (unsigned int)(qrow * D + 16 * c + 8 * half) * 2;  // rows past N: zeros
+      uint4 u = buf_load16(qres, off);
+      u.x ^= sign;
+      u.y ^= sign;
+      u.z ^= sign;
+      u.w ^= sign;
+      qf[c] = as_bf16x8(u);
+      dof[c] = as_bf16x8(buf_load16(dores, off));
     }
   }
-
-  f32x16 dv_acc[NDB], dk_acc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) {
-    dv_acc[i] = zero16();
-    dk_acc[i] = zero16();
+  float lse2 = INFINITY, dlt = 0.f;  // rows past N: P = 0
+  if (qrow < N) {
+    const float2 st = a.stats[(size_t)bh * N + qrow];
+    lse2 = st.x;
+    dlt = st.y;
   }
+  const KOffsets<D> ko = k_offsets<D>(l32, half);
+  const KtOffsets<D> kto = kt_offsets<D>(lane);
   const float c = a.c;
-  const int nqt = (N + BM - 1) / BM;
-  const int qt_first = CAUSAL ? k0 / BM : 0;
 
-  QTileRegs<D> regs;
-  if (qt_first < nqt) {
-    bwd_load_qtile<D>(a, qres, dores, hoff, qt_first * BM, tid, regs);
-    bwd_store_qtile<D>(smem, lse2, dlt, tid, regs);
-  }
-
-  for (int it = qt_first; it < nqt; ++it) {
-    const int q0 = it * BM;
-    const bool more = it + 1 < nqt;
-    __syncthreads();  // tile `it` staged; previous dS reads finished
-    if (more) bwd_load_qtile<D>(a, qres, dores, hoff, q0 + BM, tid, regs);
-
+  f32x16 dqacc[NDB];
 #pragma unroll
-    for (int qb = 0; qb < BM / 32; ++qb) {
-      const int qb0 = q0 + 32 * qb;
-      unsigned short* ds_out = smem + C::OFF_DS + (32 * qb) * C::SS + 32 * w + l32;
-      // every key of this wave after every query of the block: P = 0
-      if (CAUSAL && wave_k0 > qb0 + 31) {
+  for (int i = 0; i < NDB; ++i) dqacc[i] = zero16();
+  f32x16 s[NSB], dp[NSB];
+  bf16x8 dsf[NPT];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ds_out[acc_row_swapped(r, half) * C::SS] = 0;
-        continue;
+  for (int i = 0; i < NPT; ++i) dsf[i] = as_bf16x8(zero_uint4());
+
+  auto gemm_phase = [&](const unsigned short* kprev, const unsigned short* kcur, const unsigned short* vcur)
+                        __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    kt_tile<D, BN>(kprev, kto, dsf, dqacc);
+    qk_tile<D, BN>(kcur, ko, qf, s);
+    qk_tile<D, BN>(vcur, ko, dof, dp);
+    sched_dq_gemm<D, BN>();
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto vector_phase = [&](int t) __attribute__((always_inline)) {
+    const int kt = tile_at(t);
+    const bool masked = need_mask(kt);
+#pragma unroll
+    for (int b = 0; b < NSB; ++b) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -lse2));
+        float ds = p * (dp[b][r] - dlt);
+        if (masked) {
+          const int key = kt * BN + 32 * b + acc_row_swapped(r, half);
+          ds = (key >= N || (CAUSAL && key > qrow)) ? 0.f : ds;
+        }
+        s[b][r] = ds;
       }
-      f32x16 s = zero16(), dp = zero16();
-      const unsigned short* qrow = smem + C::OFF_Q + (32 * qb + l32) * C::RS + 8 * half;
-      const unsigned short* dorow = smem + C::OFF_DO + (32 * qb + l32) * C::RS + 8 * half;
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < NPT; ++t2) dsf[t2] = pack_bf16(s[t2 >> 1], 8 * (t2 & 1));
+  };
+
+  // Step t: buffers rotate with t mod 3.  kprev holds K(t-1), kcur K(t), vcur V(t);
+  // group B fetches K(t+1) into knext, group A V(t+2) into vnext2.
+  auto step = [&](int t, const unsigned short* kprev, const unsigned short* kcur, unsigned short* knext,
+                  const unsigned short* vcur, unsigned short* vnext2) __attribute__((always_inline)) {
+    if (grp == 0) {
+      dma_k<D, BN>(vres, vnext2, tile_at(t + 2), wg, lane);
+      gemm_phase(kprev, kcur, vcur);
+    } else {
+      dma_k<D, BN>(kres, knext, tile_at(t + 1), wg, lane);
+      if (t >= 1) vector_phase(t - 1);
+    }
+    barrier_plain();
+    if (grp == 0) {
+      if (t < ntiles) vector_phase(t);
+      wait_lgkm_vm<C::KB_PER_WAVE>();  // V(t+1) has landed
+    } else {
+      gemm_phase(kprev, kcur, vcur);
+      wait_lgkm_vm<0>();  // K(t+1) has landed
+    }
+    barrier_ring<15>();
+  };
+  for (int t = 0; t <= ntiles; t += 3) {
+    step(t, kbuf_2, kbuf_0, kbuf_1, vbuf_0, vbuf_2);
+    if (t + 1 <= ntiles) step(t + 1, kbuf_0, kbuf_1, kbuf_2, vbuf_1, vbuf_0);
+    if (t + 2 <= ntiles) step(t + 2, kbuf_1, kbuf_2, kbuf_0, vbuf_2, vbuf_1);
+  }
+  wait_dma();  // no LDS-direct load may outlive the workgroup
+
+  store_grad_rows<D>(a.dq, hoff, N, qrow, half, a.grad_bf16, dqacc, a.scale);
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV kernel: one workgroup = 128 keys of one (b, h).  Waves w and w+4 share
+// a SIMD and the 32 keys 32w .. 32w+31; they split the work by role:
+//   score wave (w < 4): S = Q K^T and dP = dO V^T for its keys (K, V as MFMA B
+//     fragments in VGPRs, one key per lane), then P = exp2(S c - lse log2 e)
+//     and dS = P (dP - D), packed to bf16 and handed over through LDS;
+//   gradient wave (w >= 4): dV^T += dO^T P and dK^T += Q^T dS for the same keys,
+//     the dO^T / Q^T operands read from the tiles with transposing LDS reads.
+// Step i: the score waves hand over tile i and run the MFMAs of tile i+1, the
+// gradient waves fetch tile i+2; then the score waves run the vector work of
+// tile i+1 while the gradient waves run the MFMAs of tile i.  Q and dO tiles
+// (64 queries, K layout) and their (lse, D) rows sit in rings of three buffers.
+// ---------------------------------------------------------------------------
+template <int D>
+struct DkvCfg : TileCfg<D, 64> {
+  static constexpr int BK = 128;  // keys per workgroup
+  static constexpr int BQ = 64;   // queries per tile
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
+  using C = DkvCfg<D>;
+  constexpr int BQ = C::BQ;
+  constexpr int NSB = C::NSB;  // 32-query blocks per tile
+  constexpr int NPT = C::NPT;  // 16-query fragments per tile
+  constexpr int NDB = D / 32;
+  __shared__ __align__(16) unsigned short qbuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short qbuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short qbuf_2[C::TILE];
+  __shared__ __align__(16) unsigned short obuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short obuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short obuf_2[C::TILE];
+  __shared__ __align__(16) float2 st_0[BQ];
+  __shared__ __align__(16) float2 st_1[BQ];
+  __shared__ __align__(16) float2 st_2[BQ];
+  __shared__ __align__(16) uint4 xch[4][2 * NPT][64];  // per SIMD: P then dS fragments, per lane
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: role branches are scalar
+  const int sw = w & 3;       // SIMD and key sub-block
+  const bool score = w < 4;   // role
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int N = a.N;
+  const int kt = (int)(blockIdx.x / a.BH);  // causal: small kt = most query tiles, launched first
+  const int bh = (int)(blockIdx.x % a.BH);
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const unsigned int head_bytes = (unsigned int)N * D * 2;
+  const BufRes qres = make_buf(a.q + hoff, head_bytes);
+  const BufRes dores = make_buf(a.dO + hoff, head_bytes);
+  const BufRes sres = make_buf(a.stats + (size_t)bh * N, (unsigned int)N * 8);
+  const int k0 = kt * C::BK;
+  const int wave_k0 = k0 + 32 * sw;
+  const int mykey = wave_k0 + l32;
+  const int nqt = (N + BQ - 1) / BQ;
+  const int t_first = CAUSAL ? k0 / BQ : 0;
+  const int T = nqt - t_first;  // >= 1: k0 < N
+
+  // tile i (queries (t_first + i) * 64 ..) into buffer set i % 3, by the gradient waves
+  auto fetch = [&](int i, unsigned short* qb, unsigned short* ob, float2* st) __attribute__((always_inline)) {
+    const int tq = t_first + i;
+    dma_k<D, BQ>(qres, qb, tq, sw, lane);
+    dma_k<D, BQ>(dores, ob, tq, sw, lane);
+    if (sw == 0 && lane < 32)  // 64 rows x 8 bytes; rows past N read as zeros
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_void_t*)st, 16, (unsigned int)(tq * BQ * 8 + 16 * lane),
+                                               0, 0, 0);
+  };
+  constexpr int LOADS = 2 * C::KB_PER_WAVE + 1;  // loads of one fetch by gradient wave 0 (the others: one fewer)
+
+  // Every buffer starts as zeros: rows past N (which the range-checked loads may
+  // leave unwritten) are multiplied by P = dS = 0 and must hold finite values.
+  for (int i = tid; i < C::TILE / 8; i += 512) {
+    reinterpret_cast<uint4*>(qbuf_0)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(qbuf_1)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(qbuf_2)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(obuf_0)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(obuf_1)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(obuf_2)[i] = zero_uint4();
+  }
+  if (tid < BQ) st_0[tid] = st_1[tid] = st_2[tid] = make_float2(0.f, 0.f);
+  barrier_lds();
+  if (!score) {
+    fetch(0, qbuf_0, obuf_0, st_0);
+    if (T > 1) {
+      fetch(1, qbuf_1, obuf_1, st_1);
+      if (sw == 0) wait_dma_but<LOADS>(); else wait_dma_but<LOADS - 1>();  // tile 1 may still be landing
+    } else {
+      wait_dma();
+    }
+  }
+  barrier_ring<15>();
+
+  const float c = a.c;
+  if (score) {
+    // ---- score wave: K and V rows of this lane's key as MFMA B fragments
+    bf16x8 kf[D / 16], vf[D / 16];
+    {
+      const BufRes kres = make_buf(a.k + hoff, head_bytes);
+      const BufRes vres = make_buf(a.v + hoff, head_bytes);
+      const unsigned int sign = a.neg ? 0x80008000u : 0u;
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
-        s = mfma32(lds_bf16x8(qrow + 16 * cc), kf[cc], s);
-        dp = mfma32(lds_bf16x8(dorow + 16 * cc), vf[cc], dp);
-      }
-      // per-register query statistics: queries 32qb + 8*half + {0..7} and +16
-      float st_l[16], st_d[16];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int base = 32 * qb + 16 * hh + 8 * half;
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lse2 + base);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lse2 + base + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dlt + base);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(dlt + base + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          st_l[8 * hh + e] = l0[e];
-          st_l[8 * hh + 4 + e] = l1[e];
-          st_d[8 * hh + e] = d0[e];
-          st_d[8 * hh + 4 + e] = d1[e];
-        }
-      }
-      const bool need_mask = (k0 + 32 * w + 31 >= N) || (CAUSAL && wave_k0 + 31 > qb0);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -st_l[r]));
-        if (need_mask) {
-          const int qidx = qb0 + acc_row_swapped(r, half);
-          const bool hide = mykey >= N || (CAUSAL && mykey > qidx);
-          p = hide ? 0.f : p;
-        }
-        s[r] = p;
-        dp[r] = p * (dp[r] - st_d[r]);
-      }
-      const bf16x8 p0 = pack_bf16(s, 0), p1 = pack_bf16(s, 8);
-      const bf16x8 d0 = pack_bf16(dp, 0), d1 = pack_bf16(dp, 8);
-      // dV += P^T dO and dK += dS^T Q (queries 32qb + 16t + 8*half + e)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const unsigned short* dot = smem + C::OFF_DOT + (32 * db + l32) * C::TS + 32 * qb + 8 * half;
-        const unsigned short* qt = smem + C::OFF_QT + (32 * db + l32) * C::TS + 32 * qb + 8 * half;
-        dv_acc[db] = mfma32(p0, lds_bf16x8(dot), dv_acc[db]);
-        dv_acc[db] = mfma32(p1, lds_bf16x8(dot + 16), dv_acc[db]);
-        dk_acc[db] = mfma32(d0, lds_bf16x8(qt), dk_acc[db]);
-        dk_acc[db] = mfma32(d1, lds_bf16x8(qt + 16), dk_acc[db]);
-      }
-      // dS (bf16) to LDS, [query][key] with queries in natural order
-      const uint4 u0 = as_uint4(d0), u1 = as_uint4(d1);
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        ds_out[acc_row_swapped(r, half) * C::SS] = bf16_lane_of(u0, r);
-        ds_out[acc_row_swapped(r + 8, half) * C::SS] = bf16_lane_of(u1, r);
+        const unsigned int off = (unsigned int)(mykey * D + 16 * cc + 8 * half) * 2;  // keys past N: zeros
+        uint4 u = buf_load16(kres, off);
+        u.x ^= sign;
+        u.y ^= sign;
+        u.z ^= sign;
+        u.w ^= sign;
+        kf[cc] = as_bf16x8(u);
+        vf[cc] = as_bf16x8(buf_load16(vres, off));
       }
     }
-    __syncthreads();  // dS complete; every wave is done with the Q / dO tile
-    if (more) bwd_store_qtile<D>(smem, lse2, dlt, tid, regs);
-
-    // dQ_tile (BM x D) += scale * dS (BM x 128 keys) K (128 keys x D): 32x32 blocks over the waves
-    constexpr int NBLK = (BM / 32) * NDB;
-    for (int blk = w; blk < NBLK; blk += 4) {
-      const int qb = blk / NDB;
-      const int db = blk % NDB;
-      f32x16 acc = zero16();
-      const unsigned short* arow = smem + C::OFF_DS + (32 * qb + l32) * C::SS + 8 * half;
-      const unsigned short* brow = smem + C::OFF_KT + (32 * db + l32) * C::KTS + 8 * half;
+    const KOffsets<D> ko = k_offsets<D>(l32, half);
+    f32x16 s[NSB], dp[NSB];
+    bf16x8 pf[NPT], dsf[NPT];
+    auto score_mfma = [&](const unsigned short* qb, const unsigned short* ob) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(1);
+      qk_tile<D, BQ>(qb, ko, kf, s);
+      qk_tile<D, BQ>(ob, ko, vf, dp);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    // P and dS of tile i (register r of block b is query 32b + acc_row_swapped(r, half))
+    auto score_vector = [&](int i, const float2* st) __attribute__((always_inline)) {
+      const int q0 = (t_first + i) * BQ;
+      const bool masked = (q0 + BQ > N) || (CAUSAL && q0 < wave_k0 + 31);
 #pragma unroll
-      for (int kc = 0; kc < BN / 16; ++kc) acc = mfma32(lds_bf16x8(arow + 16 * kc), lds_bf16x8(brow + 16 * kc), acc);
-      const int d = 32 * db + l32;
+      for (int b = 0; b < NSB; ++b) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qidx = q0 + 32 * qb + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (qidx < N) unsafeAtomicAdd(a.dq_acc + hoff + (size_t)qidx * D + d, acc[r] * a.scale);
-      }
-    }
-  }
-
-  // ---- dK, dV out: C layout has lane = d column, registers = keys
+        for (int g = 0; g < 2; ++g) {
+          // queries 32b + 16g + 8h + e, e = 0..7: four float4 reads of (lse log2 e, D) pairs
+          const float4* src = reinterpret_cast<const float4*>(st + 32 * b + 16 * g + 8 * half);
+          float2 sd[8];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int d = 32 * db + l32;
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float4 x = src[e2];
+            sd[2 * e2] = make_float2(x.x, x.y);
+            sd[2 * e2 + 1] = make_float2(x.z, x.w);
+          }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = wave_k0 + 8 * (r >> 2) + 4 * half + (r & 3);
-      if (key < N) {
-        const size_t idx = hoff + (size_t)key * D + d;
-        const float gk = dk_acc[db][r] * a.scale_abs;
-        const float gv = dv_acc[db][r];
-        if (a.grad_bf16) {
-          static_cast<unsigned short*>(a.dk)[idx] = float_to_bf16_bits(gk);
-          static_cast<unsigned short*>(a.dv)[idx] = float_to_bf16_bits(gv);
-        } else {
-          static_cast<float*>(a.dk)[idx] = gk;
-          static_cast<float*>(a.dv)[idx] = gv;
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * g + e;
+            float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -sd[e].x));
+            float ds = p * (dp[b][r] - sd[e].y);
+            if (masked) {
+              const int qi = q0 + 32 * b + acc_row_swapped(r, half);
+              const bool hide = qi >= N || (CAUSAL && mykey > qi);
+              p = hide ? 0.f : p;
+              ds = hide ? 0.f : ds;
+            }
+            s[b][r] = p;
+            dp[b][r] = ds;
+          }
         }
       }
+#pragma unroll
+      for (int t2 = 0; t2 < NPT; ++t2) {
+        pf[t2] = pack_bf16(s[t2 >> 1], 8 * (t2 & 1));
+        dsf[t2] = pack_bf16(dp[t2 >> 1], 8 * (t2 & 1));
+      }
+    };
+    auto step = [&](int i, const unsigned short* qnxt, const unsigned short* onxt, const float2* snxt)
+                    __attribute__((always_inline)) {
+#pragma unroll
+      for (int t2 = 0; t2 < NPT; ++t2) {
+        xch[sw][t2][lane] = as_uint4(pf[t2]);
+        xch[sw][NPT + t2][lane] = as_uint4(dsf[t2]);
+      }
+      if (i + 1 < T) score_mfma(qnxt, onxt);
+      barrier_ring<15>();  // the handover writes have completed
+      if (i + 1 < T) score_vector(i + 1, snxt);
+      barrier_ring<15>();
+    };
+    score_mfma(qbuf_0, obuf_0);
+    score_vector(0, st_0);
+    for (int i = 0; i < T; i += 3) {
+      step(i, qbuf_1, obuf_1, st_1);
+      if (i + 1 < T) step(i + 1, qbuf_2, obuf_2, st_2);
+      if (i + 2 < T) step(i + 2, qbuf_0, obuf_0, st_0);
     }
+  } else {
+    // ---- gradient wave: dV^T and dK^T accumulators (lane = key, registers = d)
+    const KtOffsets<D> kto = kt_offsets<D>(lane);
+    f32x16 dvacc[NDB], dkacc[NDB];
+#pragma unroll
+    for (int i = 0; i < NDB; ++i) {
+      dvacc[i] = zero16();
+      dkacc[i] = zero16();
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS for one tile
+    auto grad_mfma = [&](const unsigned short* qb, const unsigned short* ob) __attribute__((always_inline)) {
+      bf16x8 xp[NPT], xd[NPT];
+#pragma unroll
+      for (int t2 = 0; t2 < NPT; ++t2) {
+        xp[t2] = as_bf16x8(xch[sw][t2][lane]);
+        xd[t2] = as_bf16x8(xch[sw][NPT + t2][lane]);
+      }
+      __builtin_amdgcn_s_setprio(1);
+      kt_tile<D, BQ>(ob, kto, xp, dvacc);
+      kt_tile<D, BQ>(qb, kto, xd, dkacc);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    auto step = [&](int i, const unsigned short* qcur, const unsigned short* ocur, unsigned short* qfar,
+                    unsigned short* ofar, float2* sfar) __attribute__((always_inline)) {
+      if (i + 2 < T) fetch(i + 2, qfar, ofar, sfar);
+      barrier_ring<15>();
+      grad_mfma(qcur, ocur);
+      wait_lgkm_vm<0>();  // tile i+2 has landed
+      barrier_ring<15>();
+    };
+    for (int i = 0; i < T; i += 3) {
+      step(i, qbuf_0, obuf_0, qbuf_2, obuf_2, st_2);
+      if (i + 1 < T) step(i + 1, qbuf_1, obuf_1, qbuf_0, obuf_0, st_0);
+      if (i + 2 < T) step(i + 2, qbuf_2, obuf_2, qbuf_1, obuf_1, st_1);
+    }
+    wait_dma();
+    store_grad_rows<D>(a.dv, hoff, N, mykey, half, a.grad_bf16, dvacc, 1.f);
+    store_grad_rows<D>(a.dk, hoff, N, mykey, half, a.grad_bf16, dkacc, a.scale);
   }
 }
 
@@ -397,7 +551,7 @@ struct BwdF32Args {
   const float* v;
   const float* dO;
   const float* lse;
-  const float* delta;
+  const float2* stats;  // (lse log2 e, D) per row; D is used here
   float* dq;
   float* dk;
   float* dv;
@@ -442,7 +596,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dkdv_kernel(BwdF32Args a) {
     if (tid < BQ) {
       const int row = q0 + tid;
       ls[tid] = row < N ? a.lse[hoff / D + row] : -INFINITY;
-      dl[tid] = row < N ? a.delta[hoff / D + row] : 0.f;
+      dl[tid] = row < N ? a.stats[hoff / D + row].y : 0.f;
     }
     __syncthreads();
     if (key < N) {
@@ -495,7 +649,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdF32Args a) {
     g[t] = 0.f;
   }
   const float l = in ? a.lse[hoff / D + qi] : -INFINITY;
-  const float dl = in ? a.delta[hoff / D + qi] : 0.f;
+  const float dl = in ? a.stats[hoff / D + qi].y : 0.f;
   const int kend = CAUSAL ? min(N, qt * BQ + BQ) : N;
   for (int k0 = 0; k0 < kend; k0 += BK) {
     __syncthreads();
@@ -532,37 +686,36 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdF32Args a) {
 // launchers
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-static void launch_delta(const BwdParams& p, hipStream_t stream) {
+static void launch_prep(const BwdParams& p, hipStream_t stream) {
   constexpr int EPT = 16 / sizeof(T);
   constexpr int RPB = 256 / (D / EPT);
   const long long rows = (long long)p.B * p.H * p.N;
   const unsigned blocks = (unsigned)((rows + RPB - 1) / RPB);
-  hipLaunchKernelGGL((bwd_delta_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, static_cast<const T*>(p.o),
-                     static_cast<const T*>(p.dO), p.delta, rows);
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, static_cast<const T*>(p.o),
+                     static_cast<const T*>(p.dO), p.lse, reinterpret_cast<float2*>(p.stats), rows);
 }
 
 template <int D, bool CAUSAL>
-static void launch_bwd_bf16_main(const BwdParams& p, hipStream_t stream) {
-  BwdKernelArgs a;
+static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
+  BwdBf16Args a;
   a.q = static_cast<const unsigned short*>(p.q);
   a.k = static_cast<const unsigned short*>(p.k);
   a.v = static_cast<const unsigned short*>(p.v);
   a.dO = static_cast<const unsigned short*>(p.dO);
-  a.lse = p.lse;
-  a.delta = p.delta;
-  a.dq_acc = p.dq_acc;
+  a.stats = reinterpret_cast<const float2*>(p.stats);
+  a.dq = p.dq;
   a.dk = p.dk;
   a.dv = p.dv;
   a.grad_bf16 = p.grad_dtype == 1;
   a.BH = p.B * p.H;
   a.N = p.N;
-  const float sa = fabsf(p.scale);
-  a.c = fmaxf(sa * kLog2e, 0x1p-100f);
-  a.scale_abs = sa;
+  a.c = fmaxf(fabsf(p.scale) * kLog2e, 0x1p-100f);
   a.scale = p.scale;
   a.neg = p.scale < 0.f ? 1 : 0;
-  const int nkt = (p.N + 127) / 128;
-  hipLaunchKernelGGL((bwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)(nkt * a.BH)), dim3(256), 0, stream, a);
+  const unsigned nkb = (unsigned)((p.N + 127) / 128);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nkb * (unsigned)a.BH), dim3(512), 0, stream, a);
+  const unsigned nqb = (unsigned)((p.N + 255) / 256);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, 64, CAUSAL>), dim3(nqb * (unsigned)a.BH), dim3(512), 0, stream, a);
 }
 
 template <int D, bool CAUSAL>
@@ -573,7 +726,7 @@ static void launch_bwd_f32(const BwdParams& p, hipStream_t stream) {
   a.v = static_cast<const float*>(p.v);
   a.dO = static_cast<const float*>(p.dO);
   a.lse = p.lse;
-  a.delta = p.delta;
+  a.stats = reinterpret_cast<const float2*>(p.stats);
   a.dq = static_cast<float*>(p.dq);
   a.dk = static_cast<float*>(p.dk);
   a.dv = static_cast<float*>(p.dv);
@@ -587,30 +740,22 @@ static void launch_bwd_f32(const BwdParams& p, hipStream_t stream) {
 
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   (void)hipGetLastError();  // clear an error left by an earlier, unrelated HIP call
-  const long long rows = (long long)p.B * p.H * p.N;
   if (p.dtype == 0) {
     if (p.d == 64) {
-      launch_delta<float, 64>(p, stream);
+      launch_prep<float, 64>(p, stream);
       if (p.causal) launch_bwd_f32<64, true>(p, stream); else launch_bwd_f32<64, false>(p, stream);
     } else {
-      launch_delta<float, 128>(p, stream);
+      launch_prep<float, 128>(p, stream);
       if (p.causal) launch_bwd_f32<128, true>(p, stream); else launch_bwd_f32<128, false>(p, stream);
     }
     return hipGetLastError();
   }
-  const long long n4 = rows * p.d / 4;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                     reinterpret_cast<float4*>(p.dq_acc), n4);
   if (p.d == 64) {
-    launch_delta<unsigned short, 64>(p, stream);
-    if (p.causal) launch_bwd_bf16_main<64, true>(p, stream); else launch_bwd_bf16_main<64, false>(p, stream);
+    launch_prep<unsigned short, 64>(p, stream);
+    if (p.causal) launch_bwd_bf16<64, true>(p, stream); else launch_bwd_bf16<64, false>(p, stream);
   } else {
-    launch_delta<unsigned short, 128>(p, stream);
-    if (p.causal) launch_bwd_bf16_main<128, true>(p, stream); else launch_bwd_bf16_main<128, false>(p, stream);
-  }
-  if (p.grad_dtype == 1) {
-    hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream,
-                       reinterpret_cast<const float4*>(p.dq_acc), static_cast<uint2*>(p.dq), n4);
+    launch_prep<unsigned short, 128>(p, stream);
+    if (p.causal) launch_bwd_bf16<128, true>(p, stream); else launch_bwd_bf16<128, false>(p, stream);
   }
   return hipGetLastError();
 }

@@ -27,6 +27,7 @@
 
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
+#include "fa_tiles.hpp"
 
 namespace fa {
 
@@ -46,148 +47,10 @@ struct FwdKernelArgs {
 };
 
 template <int D, int BN>
-struct FwdCfg {
-  static constexpr int BM = 256;            // queries per workgroup (8 waves x 32)
-  static constexpr int NC = D / 8;          // 16-byte chunks per K / V row
-  static constexpr int RPK = 64 / NC;       // rows written by one 1 KB LDS-direct load
-  static constexpr int TILE = BN * D;       // elements of one K (or V) tile in LDS
-  static constexpr int LDS_ELEMS = 6 * TILE;  // K and V, three buffers each
-  static constexpr int NSB = BN / 32;       // 32-key S^T blocks per tile
-  static constexpr int NPT = BN / 16;       // 16-key P fragments per tile
-  static constexpr int NDB = D / 32;        // 32-wide d blocks of the output
-  static constexpr int KB_PER_WAVE = BN * D * 2 / 1024 / 4;  // 1 KB LDS-direct loads per wave per tile
-  static_assert(KB_PER_WAVE * 4 * 1024 == BN * D * 2, "a tile is a whole number of 1 KB loads per wave");
+struct FwdCfg : TileCfg<D, BN> {
+  static constexpr int BM = 256;      // queries per workgroup (8 waves x 32)
+  static constexpr int NDB = D / 32;  // 32-wide d blocks of the output
 };
-
-// ---- LDS tile layouts.  Both tiles are row-major with 16-byte chunks permuted
-// by an XOR of the row ("swizzle") so that the MFMA operand reads hit distinct
-// LDS banks:
-//   K: row R holds key swap23(R) of the tile; chunk c sits at c ^ swz_k(R).
-//      S^T reads: 32 lanes x 16 B of one chunk column over 32 consecutive rows.
-//   V: row R holds key R; chunk c sits at c ^ swz_v(R).  P.V reads use the
-//      transposing LDS read (4 rows x 16 d per 16-lane group).
-template <int D>
-__device__ __forceinline__ int swz_k(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
-}
-template <int D>
-__device__ __forceinline__ int swz_v(int row) {
-  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
-}
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// K tile kt -> LDS with 1 KB LDS-direct loads (the four waves of a group
-// cover the tile); rows past N read as zeros.
-template <int D, int BN>
-__device__ __forceinline__ void dma_k(BufRes kres, unsigned short* kbuf, int kt, int wg, int lane) {
-  using C = FwdCfg<D, BN>;
-#pragma unroll
-  for (int n = 0; n < C::KB_PER_WAVE; ++n) {
-    const int blk = wg * C::KB_PER_WAVE + n;
-    const int row = blk * C::RPK + lane / C::NC;
-    const int c = (lane % C::NC) ^ swz_k<D>(row);
-    const unsigned int off = (unsigned int)((kt * BN + swap23(row)) * D + c * 8) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (lds_void_t*)(kbuf + blk * 512), 16, off, 0, 0, 0);
-  }
-}
-
-template <int D, int BN>
-__device__ __forceinline__ void dma_v(BufRes vres, unsigned short* vbuf, int kt, int wg, int lane) {
-  using C = FwdCfg<D, BN>;
-#pragma unroll
-  for (int n = 0; n < C::KB_PER_WAVE; ++n) {
-    const int blk = wg * C::KB_PER_WAVE + n;
-    const int row = blk * C::RPK + lane / C::NC;
-    const int c = (lane % C::NC) ^ swz_v<D>(row);
-    const unsigned int off = (unsigned int)((kt * BN + row) * D + c * 8) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vres, (lds_void_t*)(vbuf + blk * 512), 16, off, 0, 0, 0);
-  }
-}
-
-// wait for this wave's LDS-direct loads (they count as vector-memory loads)
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// wait for all but the N most recent vector-memory loads (N < 16)
-template <int N>
-__device__ __forceinline__ void wait_dma_but() { __builtin_amdgcn_s_waitcnt(0x0F70 | N); }
-
-// Per-lane element offsets of the S^T operand reads (one per 16-wide d chunk).
-template <int D>
-struct KOffsets {
-  int off[D / 16];
-};
-template <int D>
-__device__ __forceinline__ KOffsets<D> k_offsets(int l32, int half) {
-  KOffsets<D> k;
-#pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) k.off[cc] = l32 * D + (((2 * cc + half) ^ swz_k<D>(l32)) * 8);
-  return k;
-}
-
-// ---- S^T = K Q^T for one key tile: lane (query l32, half h), register r of block b
-// holds key 32b + 16(r/8) + 8h + (r%8) of the tile (K rows are swap23-ordered in LDS).
-template <int D, int BN>
-__device__ __forceinline__ void qk_tile(const unsigned short* kbuf, const KOffsets<D>& ko, const bf16x8 (&qf)[D / 16],
-                                        f32x16 (&s)[FwdCfg<D, BN>::NSB]) {
-  using C = FwdCfg<D, BN>;
-#pragma unroll
-  for (int b = 0; b < C::NSB; ++b) s[b] = zero16();
-#pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) {
-#pragma unroll
-    for (int b = 0; b < C::NSB; ++b) s[b] = mfma32(lds_bf16x8(kbuf + 32 * b * D + ko.off[cc]), qf[cc], s[b]);
-  }
-}
-
-// Per-lane element offsets of the transposing V reads: base (row part) and one
-// chunk offset per 32-wide d block.
-template <int D>
-struct VOffsets {
-  int base;
-  int blk[D / 32];
-};
-template <int D>
-__device__ __forceinline__ VOffsets<D> v_offsets(int lane) {
-  VOffsets<D> v;
-  const int half = lane >> 5;
-  const int g = lane >> 4;   // 16-lane group: (half, which 16 of the 32 d)
-  const int j = lane & 15;   // source row (j/4) and 4-element column group (j%4)
-  const int dsub = g & 1;
-  const int row = 8 * half + (j >> 2);  // + 16t + 4r at the call
-  v.base = row * D + (j & 1) * 4;
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    const int c = 4 * db + 2 * dsub + ((j & 3) >> 1);
-    v.blk[db] = (c ^ swz_v<D>(row)) * 8;
-  }
-  return v;
-}
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-__device__ __forceinline__ uint2 lds_read_tr(const unsigned short* p) {
-  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)((__attribute__((address_space(3))) unsigned short*)p));
-  return __builtin_bit_cast(uint2, r);
-}
-
-// O^T += V^T P^T: lane (query l32, half h), d block db, register r holds d = 32db + 8(r/4) + 4h + r%4.
-// The V^T operand (8 keys 16t + 8h + e for d = 32db + l32) comes from two transposing reads.
-template <int D, int BN>
-__device__ __forceinline__ void pv_tile(const unsigned short* vbuf, const VOffsets<D>& vo, const bf16x8 (&pf)[BN / 16],
-                                        f32x16 (&oacc)[D / 32]) {
-#pragma unroll
-  for (int t = 0; t < BN / 16; ++t) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const unsigned short* p = vbuf + vo.base + vo.blk[db] + 16 * t * D;
-      const uint2 lo = lds_read_tr(p);
-      const uint2 hi = lds_read_tr(p + 4 * D);
-      oacc[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf[t], oacc[db]);
-    }
-  }
-}
 
 // keys past N, and under causal masking keys after the query, get -inf
 template <int BN, bool CAUSAL>
@@ -256,38 +119,6 @@ __device__ __forceinline__ void sched_gemm_phase() {
   }
 #pragma unroll
   for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-}
-
-// Barrier without a memory fence, for the mid-step switch of the two groups'
-// roles: no LDS hazard crosses it (every buffer reuse is ordered by the
-// end-of-step barrier), and a release fence here would wait for the tile fetch
-// that has just been issued.
-__device__ __forceinline__ void barrier_plain() {
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// End-of-step barrier of the tile ring: this wave's LDS reads have completed and
-// all but its N most recent LDS-direct loads have landed before it arrives.  The
-// empty asm keeps the compiler from moving memory accesses across; unlike a
-// release fence it does not drain the loads still in flight.
-template <int N>
-__device__ __forceinline__ void barrier_ring() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // lgkmcnt(0), vmcnt(N)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// Barrier that orders LDS only: prefetches from global memory stay in flight.
-__device__ __forceinline__ void barrier_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Forward kernel: one workgroup = 256 queries of one (b, h), 8 waves of 32 queries.

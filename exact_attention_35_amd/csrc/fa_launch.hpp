@@ -30,8 +30,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;   // workspace: [B, H, N] fp32
-  float* dq_acc;  // fp32 [B, H, N, d]: dq itself for fp32 gradients, else workspace
+  float* stats;  // workspace: per row of [B, H, N], the pair (lse * log2 e, D = rowsum(dO * O))
   int B, H, N, d;
   float scale;
   int causal;

@@ -85,9 +85,9 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, const unsign
                        int dtype, void* stream);
 
 /*
- * Bytes of workspace fa_bwd needs: D = rowsum(dO * O) as fp32 [B, H, N], plus an
- * fp32 [B, H, N, d] dQ accumulator when grad_dtype is FA_BF16.  Returns 0 for
- * arguments fa_bwd would reject.
+ * Bytes of workspace fa_bwd needs: 8 per row of [B, H, N] (the row's lse * log2 e
+ * and D = rowsum(dO * O), two fp32 values).  Returns 0 for arguments fa_bwd
+ * would reject.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int grad_dtype);
 
@@ -98,8 +98,8 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int grad_dtype);
  * Attention", point 2: recomputation in the backward pass); nothing N x N is
  * stored.  dq, dk, dv are written in grad_dtype (FA_F32 or FA_BF16; FA_BF16
  * requires dtype FA_BF16).  The workspace must hold fa_bwd_workspace_size()
- * bytes; its contents on entry do not matter.  dQ is accumulated with fp32
- * atomics, so its low bits may differ from run to run.
+ * bytes; its contents on entry do not matter.  Every gradient element is
+ * reduced by one thread in a fixed order: results are deterministic.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
            void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,

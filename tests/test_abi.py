@@ -119,7 +119,7 @@ def test_bwd_validation(lib):
 
 def test_workspace_size(lib):
     n = 2 * 3 * 100
-    assert lib.fa_bwd_workspace_size(2, 3, 100, 64, 0) == (n * 4 + 255) // 256 * 256
-    assert lib.fa_bwd_workspace_size(2, 3, 100, 64, 1) == (n * 4 + 255) // 256 * 256 + n * 64 * 4
+    assert lib.fa_bwd_workspace_size(2, 3, 100, 64, 0) == n * 8
+    assert lib.fa_bwd_workspace_size(2, 3, 100, 64, 1) == n * 8
     assert lib.fa_bwd_workspace_size(2, 3, 100, 32, 0) == 0
     assert lib.fa_bwd_workspace_size(0, 3, 100, 64, 0) == 0
