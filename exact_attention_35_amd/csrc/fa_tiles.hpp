@@ -26,9 +26,13 @@ struct TileCfg {
 //      Row reads: 32 lanes x 16 B of one chunk column over 32 consecutive rows.
 //   V layout: row R holds row R; chunk c sits at c ^ swz_v(R).  Read with the
 //      transposing LDS read (4 rows x 16 columns per 16-lane group).
+// K layout swizzle: a bijection on the 16 (d = 128) or 8 (d = 64, two rows per
+// 256-byte bank line) rows of a bank group, so the 16 lanes of a 16-byte row
+// read hit distinct banks; it also spreads any 4 consecutive rows x 4
+// consecutive chunks over distinct banks, which the transposing reads need.
 template <int D>
 __device__ __forceinline__ int swz_k(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int row) {
