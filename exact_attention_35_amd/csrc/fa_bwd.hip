@@ -22,6 +22,8 @@
 // (query, key) tile pair instead of five).
 #include <math.h>
 
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_launch.hpp"
 #include "fa_tiles.hpp"
@@ -263,29 +265,36 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
                         __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
     kt_tile<D, BN>(kprev, kto, dsf, dqacc);
-    qk_tile<D, BN>(kcur, ko, qf, s);
-    qk_tile<D, BN>(vcur, ko, dof, dp);
+    qk_pair_tile<D, BN>(kcur, vcur, ko, qf, dof, s, dp);
     sched_dq_gemm<D, BN>();
     __builtin_amdgcn_s_setprio(0);
   };
-  auto vector_phase = [&](int t) __attribute__((always_inline)) {
-    const int kt = tile_at(t);
-    const bool masked = need_mask(kt);
+  // the masked variant is a separate copy so that the common path has no per-element selects
+  auto vector_body = [&](int kt, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(mask_tag)::value;
 #pragma unroll
     for (int b = 0; b < NSB; ++b) {
+      // key = base + off with off = 16(r/8) + (r%8) a constant: compare off with per-lane bounds
+      const int base = kt * BN + 32 * b + 8 * half;
+      const int lim_n = N - base, lim_c = qrow - base;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -lse2));
         float ds = p * (dp[b][r] - dlt);
-        if (masked) {
-          const int key = kt * BN + 32 * b + acc_row_swapped(r, half);
-          ds = (key >= N || (CAUSAL && key > qrow)) ? 0.f : ds;
+        if (MASKED) {
+          const int off = 16 * (r >> 3) + (r & 7);
+          ds = (off >= lim_n || (CAUSAL && off > lim_c)) ? 0.f : ds;
         }
         s[b][r] = ds;
       }
     }
 #pragma unroll
     for (int t2 = 0; t2 < NPT; ++t2) dsf[t2] = pack_bf16(s[t2 >> 1], 8 * (t2 & 1));
+  };
+  auto vector_phase = [&](int t) __attribute__((always_inline)) {
+    const int kt = tile_at(t);
+    if (need_mask(kt)) vector_body(kt, std::true_type{});
+    else vector_body(kt, std::false_type{});
   };
 
   // Step t: buffers rotate with t mod 3.  kprev holds K(t-1), kcur K(t), vcur V(t);
@@ -327,11 +336,43 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
 //     and dS = P (dP - D), packed to bf16 and handed over through LDS;
 //   gradient wave (w >= 4): dV^T += dO^T P and dK^T += Q^T dS for the same keys,
 //     the dO^T / Q^T operands read from the tiles with transposing LDS reads.
-// Step i: the score waves hand over tile i and run the MFMAs of tile i+1, the
-// gradient waves fetch tile i+2; then the score waves run the vector work of
-// tile i+1 while the gradient waves run the MFMAs of tile i.  Q and dO tiles
-// (64 queries, K layout) and their (lse, D) rows sit in rings of three buffers.
+// Step i, phase a: the score waves hand over dS(i) and run the MFMAs of tile
+// i+1 while the gradient waves run dV += dO(i)^T P(i); phase b: the score waves
+// compute P(i+1), dS(i+1) and hand over P(i+1) while the gradient waves fetch
+// tile i+2 and run dK += Q(i)^T dS(i).  Q and dO tiles (64 queries, K layout)
+// and their (lse, D) rows sit in rings of three buffers.
 // ---------------------------------------------------------------------------
+// MFMA / LDS-read interleave of an MFMA phase (masks: 0x8 MFMA, 0x100 LDS read):
+// PRE reads issue first, then after each MFMA the reads of a later one, so
+// that LDS latency hides behind the MFMAs.  N1 MFMAs take one read each.
+template <int N1>
+__device__ __forceinline__ void sched_one_read_per_mfma() {
+#pragma unroll
+  for (int i = 0; i < 6; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int i = 0; i < N1 - 6; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 6; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
+// PRE single reads first (operands held for the whole phase), then N2 MFMAs
+// that take two reads each, three MFMAs ahead.
+template <int PRE, int N2>
+__device__ __forceinline__ void sched_two_reads_per_mfma() {
+#pragma unroll
+  for (int i = 0; i < PRE + 6; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int i = 0; i < N2 - 3; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
 template <int D>
 struct DkvCfg : TileCfg<D, 64> {
   static constexpr int BK = 128;  // keys per workgroup
@@ -437,14 +478,14 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
     bf16x8 pf[NPT], dsf[NPT];
     auto score_mfma = [&](const unsigned short* qb, const unsigned short* ob) __attribute__((always_inline)) {
       __builtin_amdgcn_s_setprio(1);
-      qk_tile<D, BQ>(qb, ko, kf, s);
-      qk_tile<D, BQ>(ob, ko, vf, dp);
+      qk_pair_tile<D, BQ>(qb, ob, ko, kf, vf, s, dp);
+      sched_one_read_per_mfma<2 * NSB * (D / 16)>();
       __builtin_amdgcn_s_setprio(0);
     };
     // P and dS of tile i (register r of block b is query 32b + acc_row_swapped(r, half))
-    auto score_vector = [&](int i, const float2* st) __attribute__((always_inline)) {
-      const int q0 = (t_first + i) * BQ;
-      const bool masked = (q0 + BQ > N) || (CAUSAL && q0 < wave_k0 + 31);
+    // the masked variant is a separate copy so that the common path has no per-element selects
+    auto score_body = [&](int q0, const float2* st, auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(mask_tag)::value;
 #pragma unroll
       for (int b = 0; b < NSB; ++b) {
 #pragma unroll
@@ -463,9 +504,11 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
             const int r = 8 * g + e;
             float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -sd[e].x));
             float ds = p * (dp[b][r] - sd[e].y);
-            if (masked) {
-              const int qi = q0 + 32 * b + acc_row_swapped(r, half);
-              const bool hide = qi >= N || (CAUSAL && mykey > qi);
+            if (MASKED) {
+              // query = base + off with off = 16(r/8) + (r%8) a constant
+              const int base = q0 + 32 * b + 8 * half;
+              const int off = 16 * (r >> 3) + (r & 7);
+              const bool hide = off >= N - base || (CAUSAL && off < mykey - base);
               p = hide ? 0.f : p;
               ds = hide ? 0.f : ds;
             }
@@ -480,20 +523,31 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
         dsf[t2] = pack_bf16(dp[t2 >> 1], 8 * (t2 & 1));
       }
     };
+    auto score_vector = [&](int i, const float2* st) __attribute__((always_inline)) {
+      const int q0 = (t_first + i) * BQ;
+      if ((q0 + BQ > N) || (CAUSAL && q0 < wave_k0 + 31)) score_body(q0, st, std::true_type{});
+      else score_body(q0, st, std::false_type{});
+    };
+    // Step i: phase a hands over dS(i) and runs the MFMAs of tile i+1; phase b
+    // computes P(i+1), dS(i+1) and hands over P(i+1).  Unconditional, so that no
+    // value lives across a handover: at i + 1 = T the tile is past N and every P
+    // and dS of it is masked to zero.
     auto step = [&](int i, const unsigned short* qnxt, const unsigned short* onxt, const float2* snxt)
                     __attribute__((always_inline)) {
 #pragma unroll
-      for (int t2 = 0; t2 < NPT; ++t2) {
-        xch[sw][t2][lane] = as_uint4(pf[t2]);
-        xch[sw][NPT + t2][lane] = as_uint4(dsf[t2]);
-      }
-      if (i + 1 < T) score_mfma(qnxt, onxt);
-      barrier_ring<15>();  // the handover writes have completed
-      if (i + 1 < T) score_vector(i + 1, snxt);
-      barrier_ring<15>();
+      for (int t2 = 0; t2 < NPT; ++t2) xch[sw][NPT + t2][lane] = as_uint4(dsf[t2]);
+      score_mfma(qnxt, onxt);
+      barrier_ring<15>();  // the dS handover writes have completed
+      score_vector(i + 1, snxt);
+#pragma unroll
+      for (int t2 = 0; t2 < NPT; ++t2) xch[sw][t2][lane] = as_uint4(pf[t2]);
+      barrier_ring<15>();  // the P handover writes have completed
     };
     score_mfma(qbuf_0, obuf_0);
     score_vector(0, st_0);
+#pragma unroll
+    for (int t2 = 0; t2 < NPT; ++t2) xch[sw][t2][lane] = as_uint4(pf[t2]);
+    barrier_ring<15>();
     for (int i = 0; i < T; i += 3) {
       step(i, qbuf_1, obuf_1, st_1);
       if (i + 1 < T) step(i + 1, qbuf_2, obuf_2, st_2);
@@ -508,27 +562,28 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
       dvacc[i] = zero16();
       dkacc[i] = zero16();
     }
-    // dV^T += dO^T P, dK^T += Q^T dS for one tile
-    auto grad_mfma = [&](const unsigned short* qb, const unsigned short* ob) __attribute__((always_inline)) {
-      bf16x8 xp[NPT], xd[NPT];
+    // acc^T += X^T F for one tile, F the handed-over fragments at xch[sw][f0 ..]
+    auto grad_mfma = [&](const unsigned short* xb, int f0, f32x16 (&acc)[NDB]) __attribute__((always_inline)) {
+      bf16x8 xf[NPT];
 #pragma unroll
-      for (int t2 = 0; t2 < NPT; ++t2) {
-        xp[t2] = as_bf16x8(xch[sw][t2][lane]);
-        xd[t2] = as_bf16x8(xch[sw][NPT + t2][lane]);
-      }
+      for (int t2 = 0; t2 < NPT; ++t2) xf[t2] = as_bf16x8(xch[sw][f0 + t2][lane]);
       __builtin_amdgcn_s_setprio(1);
-      kt_tile<D, BQ>(ob, kto, xp, dvacc);
-      kt_tile<D, BQ>(qb, kto, xd, dkacc);
+      kt_tile<D, BQ>(xb, kto, xf, acc);
+      sched_two_reads_per_mfma<NPT, NPT * NDB>();
       __builtin_amdgcn_s_setprio(0);
     };
+    // Step i: phase a dV += dO(i)^T P(i); phase b fetch tile i+2, dK += Q(i)^T dS(i)
     auto step = [&](int i, const unsigned short* qcur, const unsigned short* ocur, unsigned short* qfar,
                     unsigned short* ofar, float2* sfar) __attribute__((always_inline)) {
-      if (i + 2 < T) fetch(i + 2, qfar, ofar, sfar);
+      grad_mfma(ocur, 0, dvacc);
       barrier_ring<15>();
-      grad_mfma(qcur, ocur);
+      if (i + 2 < T) fetch(i + 2, qfar, ofar, sfar);
+      grad_mfma(qcur, NPT, dkacc);
       wait_lgkm_vm<0>();  // tile i+2 has landed
       barrier_ring<15>();
     };
+    wait_dma();  // tile 1 has landed
+    barrier_ring<15>();
     for (int i = 0; i < T; i += 3) {
       step(i, qbuf_0, obuf_0, qbuf_2, obuf_2, st_2);
       if (i + 1 < T) step(i + 1, qbuf_1, obuf_1, qbuf_0, obuf_0, st_0);
@@ -715,7 +770,8 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   const unsigned nkb = (unsigned)((p.N + 127) / 128);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nkb * (unsigned)a.BH), dim3(512), 0, stream, a);
   const unsigned nqb = (unsigned)((p.N + 255) / 256);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, 64, CAUSAL>), dim3(nqb * (unsigned)a.BH), dim3(512), 0, stream, a);
+  constexpr int DQ_BN = D == 128 ? 32 : 64;  // keys per dQ tile: keeps the d = 128 kernel within 256 VGPRs
+  hipLaunchKernelGGL((bwd_dq_kernel<D, DQ_BN, CAUSAL>), dim3(nqb * (unsigned)a.BH), dim3(512), 0, stream, a);
 }
 
 template <int D, bool CAUSAL>

@@ -59,8 +59,10 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[BN / 32], int k_first, int
   for (int b = 0; b < BN / 32; ++b) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int key = k_first + 32 * b + acc_row_swapped(r, half);
-      const bool hide = key >= N || (CAUSAL && key > qrow);
+      // key = base + off with off = 16(r/8) + (r%8) a constant: compare off with per-lane bounds
+      const int base = k_first + 32 * b + 8 * half;
+      const int off = 16 * (r >> 3) + (r & 7);
+      const bool hide = off >= N - base || (CAUSAL && off > qrow - base);
       s[b][r] = hide ? -INFINITY : s[b][r];
     }
   }

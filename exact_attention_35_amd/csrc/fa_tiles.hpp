@@ -10,6 +10,14 @@
 
 namespace fa {
 
+// Hide a per-lane offset from loop-invariant code motion: the addresses derived
+// from it are then formed next to their use, instead of being kept live in VGPRs
+// across a whole loop for every buffer of a ring.
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 template <int D, int BN>
 struct TileCfg {
   static constexpr int NC = D / 8;          // 16-byte chunks per row
@@ -97,10 +105,51 @@ __device__ __forceinline__ void qk_tile(const unsigned short* kbuf, const KOffse
   using C = TileCfg<D, BN>;
 #pragma unroll
   for (int b = 0; b < C::NSB; ++b) s[b] = zero16();
+  int o[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) o[cc] = fresh(ko.off[cc]);
 #pragma unroll
   for (int cc = 0; cc < D / 16; ++cc) {
 #pragma unroll
-    for (int b = 0; b < C::NSB; ++b) s[b] = mfma32(lds_bf16x8(kbuf + 32 * b * D + ko.off[cc]), qf[cc], s[b]);
+    for (int b = 0; b < C::NSB; ++b) s[b] = mfma32(lds_bf16x8(kbuf + 32 * b * D + o[cc]), qf[cc], s[b]);
+  }
+}
+
+// Two row-read tile products at once, S += X1 F1 and P += X2 F2 (both tiles in the
+// K layout, same shape), interleaved as four independent accumulator chains, with
+// the LDS operands loaded PF MFMAs ahead into a register ring.
+template <int D, int BN, int PF = 4>
+__device__ __forceinline__ void qk_pair_tile(const unsigned short* buf1, const unsigned short* buf2,
+                                             const KOffsets<D>& ko, const bf16x8 (&f1)[D / 16],
+                                             const bf16x8 (&f2)[D / 16], f32x16 (&s1)[BN / 32],
+                                             f32x16 (&s2)[BN / 32]) {
+  constexpr int NSB = BN / 32;
+  constexpr int NM = 2 * NSB * (D / 16);
+  // MFMA m: chunk cc = m / (2 NSB), block b = (m / 2) % NSB, tile (m % 2)
+  int o[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) o[cc] = fresh(ko.off[cc]);
+  auto operand = [&](int m) __attribute__((always_inline)) -> bf16x8 {
+    const int cc = m / (2 * NSB);
+    const int b = (m >> 1) % NSB;
+    return lds_bf16x8(((m & 1) ? buf2 : buf1) + 32 * b * D + o[cc]);
+  };
+#pragma unroll
+  for (int b = 0; b < NSB; ++b) {
+    s1[b] = zero16();
+    s2[b] = zero16();
+  }
+  bf16x8 ring[PF];
+#pragma unroll
+  for (int m = 0; m < PF; ++m) ring[m] = operand(m);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const bf16x8 x = ring[m % PF];
+    if (m + PF < NM) ring[m % PF] = operand(m + PF);
+    const int cc = m / (2 * NSB);
+    const int b = (m >> 1) % NSB;
+    if (m & 1) s2[b] = mfma32(x, f2[cc], s2[b]);
+    else s1[b] = mfma32(x, f1[cc], s1[b]);
   }
 }
 
@@ -141,11 +190,14 @@ __device__ __forceinline__ uint2 lds_read_tr(const unsigned short* p) {
 template <int D, int BN>
 __device__ __forceinline__ void pv_tile(const unsigned short* vbuf, const VOffsets<D>& vo, const bf16x8 (&pf)[BN / 16],
                                         f32x16 (&oacc)[D / 32]) {
+  int o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = fresh(vo.base + vo.blk[db]);
 #pragma unroll
   for (int t = 0; t < BN / 16; ++t) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const unsigned short* p = vbuf + vo.base + vo.blk[db] + 16 * t * D;
+      const unsigned short* p = vbuf + o[db] + 16 * t * D;
       const uint2 lo = lds_read_tr(p);
       const uint2 hi = lds_read_tr(p + 4 * D);
       oacc[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf[t], oacc[db]);
@@ -187,12 +239,18 @@ __device__ __forceinline__ KtOffsets<D> kt_offsets(int lane) {
 template <int D, int BN>
 __device__ __forceinline__ void kt_tile(const unsigned short* buf, const KtOffsets<D>& o, const bf16x8 (&fr)[BN / 16],
                                         f32x16 (&acc)[D / 32]) {
+  int lo_off[D / 32], hi_off[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    lo_off[db] = fresh(o.lo[db]);
+    hi_off[db] = fresh(o.hi[db]);
+  }
 #pragma unroll
   for (int t = 0; t < BN / 16; ++t) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const uint2 lo = lds_read_tr(buf + 16 * t * D + o.lo[db]);
-      const uint2 hi = lds_read_tr(buf + 16 * t * D + o.hi[db]);
+      const uint2 lo = lds_read_tr(buf + 16 * t * D + lo_off[db]);
+      const uint2 hi = lds_read_tr(buf + 16 * t * D + hi_off[db]);
       acc[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), fr[t], acc[db]);
     }
   }
