@@ -321,25 +321,27 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   };
 
   // Step t.  Buffers rotate with t mod 3: kcur holds K(t), vprev V(t-1); at the
-  // top of phase 2t group A starts fetching V(t+1) into vnext and group B
+  // top of its MFMA phase group A starts fetching V(t+1) into vnext and group B
   // K(t+2) into knext2 (steps past the end fetch the last tile again, so every
   // step issues the same number of loads).  At the end of the step each wave
   // waits for the loads it issued one step earlier, which the next step reads.
   auto step = [&](int t, const unsigned short* kcur, unsigned short* knext2, const unsigned short* vprev,
                   unsigned short* vnext) __attribute__((always_inline)) {
-    // phase 2t: A fetches V(t+1) and runs G(t); B fetches K(t+2) and runs S(t-1)
+    // phase 2t: A fetches V(t+1) and runs G(t); B runs S(t-1).  Each group issues
+    // its tile loads in its MFMA phase, where they cost nothing: issued next to
+    // the vector work of a softmax phase they would slow it down.
     if (grp == 0) {
       dma_v<D, BN>(vres, vnext, tile_at(t + 1), wg, lane);
       gemm_phase(t, kcur, vprev);
     } else {
-      dma_k<D, BN>(kres, knext2, tile_at(t + 2), wg, lane);
       if (t >= 1) softmax_phase();
     }
     barrier_plain();
-    // phase 2t+1: A runs S(t); B runs G(t)
+    // phase 2t+1: A runs S(t); B fetches K(t+2) and runs G(t)
     if (grp == 0) {
       if (t < ntiles) softmax_phase();
     } else {
+      dma_k<D, BN>(kres, knext2, tile_at(t + 2), wg, lane);
       gemm_phase(t, kcur, vprev);
     }
     barrier_ring<C::KB_PER_WAVE>();
