@@ -14,8 +14,6 @@ constexpr long long kMaxGrid = 0x7fffffffLL;
 constexpr size_t kLdsBytes = 160 * 1024;  // gfx950 LDS per workgroup
 // static LDS of the bf16 forward: K and V tiles of 16 KB, three buffers each, plus bookkeeping
 constexpr size_t kFwdStaticLds = (size_t)6 * 16384 + 64;
-// key tiles per 128-key mask column in the bf16 forward (64-key tiles at d = 128)
-constexpr size_t fwd_tiles_per_mask_col(int d) { return d == 128 ? 2 : 1; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -68,8 +66,8 @@ int fwd_impl(const void* q, const void* k, const void* v, const unsigned char* m
   if (sparse) {
     if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     const size_t nb = ((size_t)N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
-    // the kernel lists the visited key tiles (uint16 each) in dynamic LDS
-    const size_t list_bytes = (nb * fwd_tiles_per_mask_col(d) * 2 + 15) & ~(size_t)15;
+    // the kernel lists the kept mask columns of its two mask rows (uint16 each) in dynamic LDS
+    const size_t list_bytes = (2 * nb * 2 + 15) & ~(size_t)15;
     if (kFwdStaticLds + list_bytes > kLdsBytes) return FA_ERR_UNSUPPORTED;
     const Range rm = range_of(mask, nb * nb);
     if (overlap(rm, ro) || (lse && overlap(rm, range_of(lse, n * 4)))) return FA_ERR_INVALID_ARG;

@@ -131,6 +131,11 @@ __device__ __forceinline__ void sched_gemm_phase() {
 // The MFMA phase runs at raised wave priority so that its MFMAs issue first.
 // Tiles arrive by LDS-direct loads into a ring of three buffers, two steps
 // ahead of their use (group A fetches V, group B fetches K).
+// Block-sparse: the 256 queries span two 128-row mask rows, and SIMDs 0-1 serve
+// the first, SIMDs 2-3 the second.  Each half walks the key tiles of its own
+// mask row through its own half of every ring buffer (two waves per group load
+// a tile), so that neither pays for the other's tiles; both run the same number
+// of steps (the longer list) and the other half idles through the rest.
 template <int D, int BN, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   using C = FwdCfg<D, BN>;
@@ -138,16 +143,19 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   constexpr int NSB = C::NSB;
   constexpr int NPT = C::NPT;
   constexpr int NDB = C::NDB;
+  constexpr int HT = SPARSE ? 2 : 1;                // independent tile streams
+  constexpr int NW = 4 / HT;                        // waves of a group that load one tile
+  constexpr int LPW = C::TILE * 2 / 1024 / NW;      // 1 KB loads per wave per tile
   // separate arrays (not one): the compiler then knows that LDS reads of one
   // buffer do not depend on LDS-direct loads still landing in another
-  __shared__ __align__(16) unsigned short kbuf_0[C::TILE];
-  __shared__ __align__(16) unsigned short kbuf_1[C::TILE];
-  __shared__ __align__(16) unsigned short kbuf_2[C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_0[C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_1[C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_2[C::TILE];
-  extern __shared__ __align__(16) unsigned short tile_list[];  // SPARSE only
-  __shared__ int list_len;
+  __shared__ __align__(16) unsigned short kbuf_0[HT * C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_1[HT * C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_2[HT * C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_0[HT * C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_1[HT * C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_2[HT * C::TILE];
+  extern __shared__ __align__(16) unsigned short col_list[];  // SPARSE: two lists of mask columns
+  __shared__ int list_len[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -178,53 +186,58 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   // query blocks interleave between the groups so that causal work is balanced
   const int wave_q0 = q_first + 32 * (2 * wg + grp);
   const int qrow = wave_q0 + l32;
+  const int hs = SPARSE ? (wg >> 1) : 0;  // this wave's tile stream
+  const int wi = SPARSE ? (wg & 1) : wg;  // this wave's share of a tile load
+  unsigned short* const kb0 = kbuf_0 + hs * C::TILE;
+  unsigned short* const kb1 = kbuf_1 + hs * C::TILE;
+  unsigned short* const kb2 = kbuf_2 + hs * C::TILE;
+  unsigned short* const vb0 = vbuf_0 + hs * C::TILE;
+  unsigned short* const vb1 = vbuf_1 + hs * C::TILE;
+  unsigned short* const vb2 = vbuf_2 + hs * C::TILE;
 
-  // ---- which key tiles this workgroup visits (a 256-query block spans two mask rows)
-  int ntiles;
+  // ---- which key tiles this wave's stream visits
+  int ntiles, nsteps;
   if (SPARSE) {
     constexpr int R = 128 / BN;  // key tiles per mask column
-    const int r0 = 2 * qt;
-    const int r1 = min(2 * qt + 1, a.nb - 1);
-    const unsigned char* m0 = a.mask + (size_t)r0 * a.nb;
-    const unsigned char* m1 = a.mask + (size_t)r1 * a.nb;
-    const int ncol = CAUSAL ? min(a.nb, r1 + 1) : a.nb;
-    const int nkt = (N + BN - 1) / BN;
-    if (w == 0) {
+    const int nb = a.nb;
+    if (w < 2) {  // wave h lists the columns kept by mask row 2 qt + h
+      const int r = 2 * qt + w;
+      const int ncol = r >= nb ? 0 : (CAUSAL ? r + 1 : nb);
+      const unsigned char* mrow = a.mask + (size_t)min(r, nb - 1) * nb;
       int cnt = 0;
       for (int base = 0; base < ncol; base += 64) {
         const int col = base + lane;
-        const bool on = col < ncol && (m0[col] != 0 || m1[col] != 0);
+        const bool on = col < ncol && mrow[col] != 0;
         const unsigned long long bal = __ballot(on);
-        if (on) {
-          const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
-#pragma unroll
-          for (int r = 0; r < R; ++r) tile_list[pos * R + r] = (unsigned short)(col * R + r);
-        }
+        if (on) col_list[w * nb + cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)col;
         cnt += __popcll(bal);
       }
-      if (lane == 0) {
-        int len = cnt * R;
-        while (len > 0 && (int)tile_list[len - 1] >= nkt) --len;  // tiles past N (last column only)
-        list_len = len;
-      }
+      if (lane == 0) list_len[w] = cnt;
     }
     __syncthreads();
-    ntiles = list_len;
+    // tiles of a stream: R per listed column, minus those of the last column past N
+    auto tiles_of = [&](int h) __attribute__((always_inline)) -> int {
+      const int len = list_len[h];
+      int n = len * R;
+      if (len > 0 && col_list[h * nb + len - 1] == nb - 1) n -= R - ((N - (nb - 1) * 128 + BN - 1) / BN);
+      return n;
+    };
+    ntiles = tiles_of(hs);
+    nsteps = max(tiles_of(0), tiles_of(1));
   } else {
     const int kend = CAUSAL ? min(N, q_first + BM) : N;
     ntiles = (kend + BN - 1) / BN;
+    nsteps = ntiles;
   }
   auto tile_at = [&](int t) __attribute__((always_inline)) -> int {  // steps past the end repeat the last tile
     const int tt = min(t, ntiles - 1);
-    return SPARSE ? (int)tile_list[tt] : tt;
+    if (!SPARSE) return tt;
+    constexpr int R = 128 / BN;
+    return (int)col_list[hs * a.nb + tt / R] * R + tt % R;
   };
-  // this wave's own mask row (block-sparse: the two 128-row halves differ)
-  const unsigned char* my_mrow = SPARSE ? a.mask + (size_t)min(wave_q0 / 128, a.nb - 1) * a.nb : nullptr;
   auto need_mask = [&](int kt) __attribute__((always_inline)) -> bool {
     const int k_first = kt * BN;
-    bool m = (k_first + BN > N) || (CAUSAL && k_first + BN - 1 > wave_q0);
-    if (SPARSE) m = m || my_mrow[k_first / 128] == 0;
-    return m;
+    return (k_first + BN > N) || (CAUSAL && k_first + BN - 1 > wave_q0);
   };
 
   // ---- this lane's query row as MFMA B fragments (d = 16c + 8*half .. +7)
@@ -260,7 +273,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   // V buffers start as zeros: the first MFMA phase multiplies buffer 2 by P = 0,
   // and key rows past N (which the range-checked loads may leave unwritten) must
   // hold finite values, since they are multiplied by P = 0 as well
-  for (int i = tid; i < C::TILE / 8; i += 512) {
+  for (int i = tid; i < HT * C::TILE / 8; i += 512) {
     reinterpret_cast<uint4*>(vbuf_0)[i] = zero_uint4();
     reinterpret_cast<uint4*>(vbuf_1)[i] = zero_uint4();
     reinterpret_cast<uint4*>(vbuf_2)[i] = zero_uint4();
@@ -268,14 +281,14 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   barrier_lds();
   if (ntiles > 0) {
     if (grp == 1) {
-      dma_k<D, BN>(kres, kbuf_0, tile_at(0), wg, lane);
-      dma_k<D, BN>(kres, kbuf_1, tile_at(1), wg, lane);
+      dma_k<D, BN, NW>(kres, kb0, tile_at(0), wi, lane);
+      dma_k<D, BN, NW>(kres, kb1, tile_at(1), wi, lane);
     } else {
-      dma_v<D, BN>(vres, vbuf_0, tile_at(0), wg, lane);
+      dma_v<D, BN, NW>(vres, vb0, tile_at(0), wi, lane);
       wait_dma();
     }
   }
-  barrier_ring<C::KB_PER_WAVE>();  // K(1) may still be landing
+  barrier_ring<LPW>();  // K(1) may still be landing
 
   // Branch-free so that the LDS reads run ahead of the MFMAs: at t = 0 the P.V
   // product uses P = 0 and at t = ntiles the S^T of a stale tile is never used.
@@ -288,12 +301,6 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
       const int kt = tile_at(t);
       if (need_mask(kt)) {
         mask_tile<BN, CAUSAL>(s, kt * BN, qrow, N, half);
-        if (SPARSE && my_mrow[(kt * BN) / 128] == 0) {
-#pragma unroll
-          for (int b = 0; b < NSB; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[b][r] = -INFINITY;
-        }
       }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -330,27 +337,34 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
     // phase 2t: A fetches V(t+1) and runs G(t); B runs S(t-1).  Each group issues
     // its tile loads in its MFMA phase, where they cost nothing: issued next to
     // the vector work of a softmax phase they would slow it down.
+    // (a block-sparse stream that has run out of tiles only keeps the barriers)
+    const bool active = ntiles > 0 && t <= ntiles;
     if (grp == 0) {
-      dma_v<D, BN>(vres, vnext, tile_at(t + 1), wg, lane);
-      gemm_phase(t, kcur, vprev);
+      if (active) {
+        dma_v<D, BN, NW>(vres, vnext, tile_at(t + 1), wi, lane);
+        gemm_phase(t, kcur, vprev);
+      }
     } else {
-      if (t >= 1) softmax_phase();
+      if (t >= 1 && t - 1 < ntiles) softmax_phase();
     }
     barrier_plain();
     // phase 2t+1: A runs S(t); B fetches K(t+2) and runs G(t)
     if (grp == 0) {
       if (t < ntiles) softmax_phase();
     } else {
-      dma_k<D, BN>(kres, knext2, tile_at(t + 2), wg, lane);
-      gemm_phase(t, kcur, vprev);
+      if (active) {
+        dma_k<D, BN, NW>(kres, knext2, tile_at(t + 2), wi, lane);
+        gemm_phase(t, kcur, vprev);
+      }
     }
-    barrier_ring<C::KB_PER_WAVE>();
+    barrier_ring<LPW>();
   };
-  // with no key tile at all (an empty block-sparse row) O = 0 and lse = -inf
-  for (int t = 0; ntiles > 0 && t <= ntiles; t += 3) {
-    step(t, kbuf_0, kbuf_2, vbuf_2, vbuf_1);
-    if (t + 1 <= ntiles) step(t + 1, kbuf_1, kbuf_0, vbuf_0, vbuf_2);
-    if (t + 2 <= ntiles) step(t + 2, kbuf_2, kbuf_1, vbuf_1, vbuf_0);
+  // Every wave runs the same steps (the barriers need it); a stream without any
+  // key tile (an empty block-sparse row) stays inactive: O = 0 and lse = -inf.
+  for (int t = 0; nsteps > 0 && t <= nsteps; t += 3) {
+    step(t, kb0, kb2, vb2, vb1);
+    if (t + 1 <= nsteps) step(t + 1, kb1, kb0, vb0, vb2);
+    if (t + 2 <= nsteps) step(t + 2, kb2, kb1, vb1, vb0);
   }
   wait_dma();  // no LDS-direct load may outlive the workgroup
 
@@ -484,7 +498,7 @@ static hipError_t launch_fwd_bf16_t(const FwdParams& p, hipStream_t stream) {
   const int nqt = (p.N + 255) / 256;
   const dim3 grid((unsigned)(nqt * a.BH));
   size_t dyn = 0;
-  if (SPARSE) dyn = (((size_t)a.nb * (128 / BN) * sizeof(unsigned short)) + 15) & ~(size_t)15;
+  if (SPARSE) dyn = ((2 * (size_t)a.nb * sizeof(unsigned short)) + 15) & ~(size_t)15;
   if (SPARSE && dyn > 0) {
     // the tile list lives in dynamic LDS next to the static tiles
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, BN, CAUSAL, SPARSE>),
@@ -518,16 +532,17 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     if (p.d == 64) return p.causal ? launch_fwd_f32_t<64, true>(p, stream) : launch_fwd_f32_t<64, false>(p, stream);
     return p.causal ? launch_fwd_f32_t<128, true>(p, stream) : launch_fwd_f32_t<128, false>(p, stream);
   }
+  // block-sparse: 8 KB tiles (64 keys at d = 64, 32 at d = 128), two streams per workgroup
   if (p.d == 64) {
     if (sparse)
-      return p.causal ? launch_fwd_bf16_t<64, 128, true, true>(p, stream)
-                      : launch_fwd_bf16_t<64, 128, false, true>(p, stream);
+      return p.causal ? launch_fwd_bf16_t<64, 64, true, true>(p, stream)
+                      : launch_fwd_bf16_t<64, 64, false, true>(p, stream);
     return p.causal ? launch_fwd_bf16_t<64, 128, true, false>(p, stream)
                     : launch_fwd_bf16_t<64, 128, false, false>(p, stream);
   }
   if (sparse)
-    return p.causal ? launch_fwd_bf16_t<128, 64, true, true>(p, stream)
-                    : launch_fwd_bf16_t<128, 64, false, true>(p, stream);
+    return p.causal ? launch_fwd_bf16_t<128, 32, true, true>(p, stream)
+                    : launch_fwd_bf16_t<128, 32, false, true>(p, stream);
   return p.causal ? launch_fwd_bf16_t<128, 64, true, false>(p, stream)
                   : launch_fwd_bf16_t<128, 64, false, false>(p, stream);
 }

@@ -49,14 +49,16 @@ __device__ __forceinline__ int swz_v(int row) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// K tile kt -> LDS with 1 KB LDS-direct loads (the four waves of a group
-// cover the tile); rows past N read as zeros.
-template <int D, int BN>
-__device__ __forceinline__ void dma_k(BufRes kres, unsigned short* kbuf, int kt, int wg, int lane) {
+// Tile kt -> LDS with 1 KB LDS-direct loads; NW waves (index wi) cover the tile
+// together.  Rows past the end of the buffer resource read as zeros.
+template <int D, int BN, int NW = 4>
+__device__ __forceinline__ void dma_k(BufRes kres, unsigned short* kbuf, int kt, int wi, int lane) {
   using C = TileCfg<D, BN>;
+  constexpr int LPW = BN * D * 2 / 1024 / NW;  // loads per wave
+  static_assert(LPW * NW * 1024 == BN * D * 2, "a tile is a whole number of 1 KB loads per wave");
 #pragma unroll
-  for (int n = 0; n < C::KB_PER_WAVE; ++n) {
-    const int blk = wg * C::KB_PER_WAVE + n;
+  for (int n = 0; n < LPW; ++n) {
+    const int blk = wi * LPW + n;
     const int row = blk * C::RPK + lane / C::NC;
     const int c = (lane % C::NC) ^ swz_k<D>(row);
     const unsigned int off = (unsigned int)((kt * BN + swap23(row)) * D + c * 8) * 2;
@@ -64,12 +66,14 @@ __device__ __forceinline__ void dma_k(BufRes kres, unsigned short* kbuf, int kt,
   }
 }
 
-template <int D, int BN>
-__device__ __forceinline__ void dma_v(BufRes vres, unsigned short* vbuf, int kt, int wg, int lane) {
+template <int D, int BN, int NW = 4>
+__device__ __forceinline__ void dma_v(BufRes vres, unsigned short* vbuf, int kt, int wi, int lane) {
   using C = TileCfg<D, BN>;
+  constexpr int LPW = BN * D * 2 / 1024 / NW;
+  static_assert(LPW * NW * 1024 == BN * D * 2, "a tile is a whole number of 1 KB loads per wave");
 #pragma unroll
-  for (int n = 0; n < C::KB_PER_WAVE; ++n) {
-    const int blk = wg * C::KB_PER_WAVE + n;
+  for (int n = 0; n < LPW; ++n) {
+    const int blk = wi * LPW + n;
     const int row = blk * C::RPK + lane / C::NC;
     const int c = (lane % C::NC) ^ swz_v<D>(row);
     const unsigned int off = (unsigned int)((kt * BN + row) * D + c * 8) * 2;

@@ -57,7 +57,7 @@ enum fa_status {
   FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}; N * d * 4 > 2^31 - 1 (one head's slice is
                               addressed with 32-bit byte offsets); fp32 with block-sparse;
                               a block-sparse N whose tile list does not fit in LDS
-                              (N above about 4.19M at d = 64, 2.09M at d = 128); bf16 gradients for
+                              (N above about 2.09M); bf16 gradients for
                               fp32 inputs */
   FA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than fa_bwd_workspace_size() */
   FA_ERR_HIP = -4          /* a HIP launch reported an error */

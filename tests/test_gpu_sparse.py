@@ -45,6 +45,8 @@ def test_random_masks(d, causal):
         mask = inputs.random_block_mask(n, nb, 0.4, causal)
         if nb > 2:
             mask[1, :] = 0  # a tile row with no visible key: O = 0, lse = -inf
+        if nb > 3:
+            mask[2, :] = 0  # the first of a workgroup's two mask rows empty, the second not
         scale = api.default_scale(d)
         o, lse = run_sparse(q, k, v, mask, scale, causal)
         ro, rl = oracle.forward(q, k, v, scale, causal, mask, inputs.MASK_BLOCK)
@@ -55,7 +57,11 @@ def test_random_masks(d, causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_full_masks_equal_dense(d):
-    """All-ones mask == dense; lower-triangular all-ones mask + causal == causal dense (same kernel arithmetic)."""
+    """All-ones mask == dense; lower-triangular all-ones mask + causal == causal dense.
+
+    The block-sparse kernel walks smaller key tiles than the dense one, so the two
+    agree to rounding (each is checked against the oracle), not bit for bit.
+    """
     n = 700
     nb = -(-n // 128)
     announce(f"sparse == dense d={d}")
@@ -65,4 +71,7 @@ def test_full_masks_equal_dense(d):
         os_, ls_ = run_sparse(q, k, v, mask, 0.1, causal)
         o, lse = api.forward(dev(q, BF), dev(k, BF), dev(v, BF), 0.1, causal)
         torch.cuda.synchronize()
-        assert np.array_equal(os_, host(o)) and np.array_equal(ls_, host(lse)), (d, causal)
+        ro, rl = oracle.forward(q, k, v, 0.1, causal)
+        for oo, ll in ((os_, ls_), (host(o), host(lse))):
+            assert max_err(oo, ro) <= TOL_BF16 and max_err(ll, rl) <= TOL_LSE, (d, causal)
+        assert max_err(os_, host(o)) <= TOL_BF16 and max_err(ls_, host(lse)) <= TOL_LSE, (d, causal)
