@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--workload", default="long_s16k_d128")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the fp64 oracle")
     ap.add_argument("--no-extra", action="store_true", help="skip the per-workload kernel table")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: fwd/bwd TFLOP/s over N = 512..64K, d = 64/128, causal 0/1 "
+                         "(H = 16, B = max(1, 32768 / N)), printed as one JSON line")
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="print a text summary of the rocprofv3 CSV output under DIR and exit")
     ap.add_argument("--only", choices=["step", "fwd", "bwd", "copy"], default="step",
@@ -117,6 +120,44 @@ def kernel_table():
         rows[name] = {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in entry.items()}
         del tq, tk, tv
         torch.cuda.empty_cache()
+    return rows
+
+
+def sweep():
+    """TFLOP/s of fa_fwd and fa_bwd over the metric's range of sequence lengths and head dims.
+
+    H = 16 and B = max(1, 32768 / N) heads of iid N(0, 1) bf16 activations drawn on
+    the device from a seeded generator (only timed, never checked here).
+    """
+    import torch
+
+    from exact_attention_35_amd import api
+
+    rows = []
+    gen = torch.Generator(device="cuda:0")
+    for d in (64, 128):
+        for causal in (False, True):
+            for N in (512, 1024, 2048, 4096, 8192, 16384, 32768, 65536):
+                B, H = max(1, 32768 // N), 16
+                gen.manual_seed(35 * 1000003 + N * 7 + d + int(causal))
+                shape = (B, H, N, d)
+                q, k, v, do = (torch.randn(shape, generator=gen, device="cuda:0", dtype=torch.float32)
+                               .to(torch.bfloat16) for _ in range(4))
+                o, lse = api.forward(q, k, v, None, causal)
+                ws = torch.empty(api.bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device="cuda:0")
+                n_it = max(3, min(20, int(2e12 / (4.0 * B * H * N * N * d))))
+                f_ms = time_calls(lambda: api.forward(q, k, v, None, causal, out=o, lse_out=lse), n_it)
+                b_ms = time_calls(lambda: api.backward(q, k, v, o, lse, do, None, causal, workspace=ws), n_it)
+                fl = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
+                rows.append({"N": N, "d": d, "causal": causal, "B": B, "H": H,
+                             "fwd_ms": round(f_ms, 4), "fwd_tflops": round(fl / f_ms / 1e9, 1),
+                             "fwd_frac_peak": round(fl / f_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                             "bwd_ms": round(b_ms, 4), "bwd_tflops": round(2.5 * fl / b_ms / 1e9, 1),
+                             "bwd_frac_peak": round(2.5 * fl / b_ms / 1e9 / PEAK_BF16_TFLOPS, 4)})
+                print(f"sweep N={N} d={d} causal={causal}: fwd {rows[-1]['fwd_tflops']} TFLOP/s, "
+                      f"bwd {rows[-1]['bwd_tflops']} TFLOP/s", file=sys.stderr, flush=True)
+                del q, k, v, do, o, lse, ws
+                torch.cuda.empty_cache()
     return rows
 
 
@@ -235,6 +276,10 @@ def main():
 
     from exact_attention_35_amd import api, inputs
 
+    if args.sweep:
+        print(json.dumps({"metric": METRIC, "unit": "TFLOP/s", "dtype": "bf16", "data": "synthetic",
+                          "peak": PEAK_BF16_TFLOPS, "sweep": sweep()}), flush=True)
+        return
     if args.only == "copy":
         copy_calibration(args)
         return
