@@ -107,6 +107,14 @@ def kernel_table():
             tm = torch.from_numpy(mask).to("cuda:0")
             ms = time_calls(lambda: api.forward_blocksparse(tq, tk, tv, tm, w.scale, w.causal), 10)
             entry.update(fwd_ms=ms, fwd_tflops=flops_fwd(w, dens) / ms / 1e9, density=dens)
+            # block-sparse backward on the same mask
+            o, lse = api.forward_blocksparse(tq, tk, tv, tm, w.scale, w.causal)
+            tdo = to_dev(inputs.draw(w.index, inputs.SLOT_DO, w.shape), torch.bfloat16)
+            ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda:0")
+            bms = time_calls(lambda: api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws,
+                                                  block_mask=tm), 5)
+            entry.update(bwd_ms=bms, bwd_tflops=2.5 * flops_fwd(w, dens) / bms / 1e9)
+            del o, lse, tdo, ws
         else:
             ms = time_calls(lambda: api.forward(tq, tk, tv, w.scale, w.causal), 20)
             entry.update(fwd_ms=ms, fwd_tflops=flops_fwd(w) / ms / 1e9)

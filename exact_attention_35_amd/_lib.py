@@ -20,7 +20,8 @@ FA_F32 = 0
 FA_BF16 = 1
 FA_MASK_BLOCK = 128
 
-EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_size", "fa_bwd", "fa_status_string", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_blocksparse", "fa_bwd_workspace_size", "fa_bwd", "fa_bwd_blocksparse",
+           "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -63,6 +64,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.restype = _i
     lib.fa_bwd.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _i, _i,
                            _vp, ctypes.c_size_t, _vp]
+    lib.fa_bwd_blocksparse.restype = _i
+    lib.fa_bwd_blocksparse.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _f, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
     _lib = lib
     return lib
 

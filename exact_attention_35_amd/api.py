@@ -88,12 +88,26 @@ def bwd_workspace_size(B: int, H: int, N: int, d: int, grad_dtype: torch.dtype =
     return int(_lib.load().fa_bwd_workspace_size(B, H, N, d, _DTYPES[grad_dtype]))
 
 
+def _check_mask(block_mask: torch.Tensor, N: int, device: torch.device) -> None:
+    nb = -(-N // _lib.FA_MASK_BLOCK)
+    if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != (nb, nb):
+        raise ValueError(f"block_mask must be uint8 [{nb}, {nb}]")
+    if not block_mask.is_contiguous() or block_mask.device != device:
+        raise ValueError("block_mask must be contiguous and on the same GPU as q")
+
+
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
              do: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
-             grad_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None
-             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Gradients (dq, dk, dv) of sum(do * o), in grad_dtype (float32 by default)."""
+             grad_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None,
+             block_mask: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients (dq, dk, dv) of sum(do * o), in grad_dtype (float32 by default).
+
+    With block_mask (uint8 [ceil(N/128), ceil(N/128)], as for forward_blocksparse) this is
+    the block-sparse backward, fa_bwd_blocksparse.
+    """
     B, H, N, d = _check_qkv(q, k, v)
+    if block_mask is not None:
+        _check_mask(block_mask, N, q.device)
     for name, t in (("o", o), ("do", do)):
         if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
             raise ValueError(f"{name} must match q in shape, dtype and device, and be contiguous")
@@ -108,12 +122,18 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     need = bwd_workspace_size(B, H, N, d, grad_dtype)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    lib = _lib.load()
+    tail = (B, H, N, d, scale, int(bool(causal)), _DTYPES[q.dtype], _DTYPES[grad_dtype], workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
     with torch.cuda.device(q.device):
-        st = _lib.load().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, scale,
-                                int(bool(causal)), _DTYPES[q.dtype], _DTYPES[grad_dtype], workspace.data_ptr(),
-                                workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
-    _lib.check(st, "fa_bwd")
+        if block_mask is None:
+            st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), *tail)
+        else:
+            st = lib.fa_bwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), block_mask.data_ptr(),
+                                        o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                        dv.data_ptr(), *tail)
+    _lib.check(st, "fa_bwd" if block_mask is None else "fa_bwd_blocksparse")
     return dq, dk, dv
 
 

@@ -131,9 +131,17 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int grad_dtype) {
   return n * 8;  // per row: (lse * log2 e, D), two fp32
 }
 
-int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
-           void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype, int grad_dtype,
-           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// static LDS of the block-sparse backward kernels (tile rings, hand-over buffers, bookkeeping)
+constexpr size_t bwd_dkdv_static_lds(int d) { return d == 128 ? 132608 + 64 : 83456 + 64; }
+constexpr size_t kBwdDqStaticLds = (size_t)6 * 16384 + 64;
+
+int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* mask, const void* o, const float* lse,
+             const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
+             int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream, bool sparse) {
   int st = check_common(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (grad_dtype != FA_F32 && grad_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
@@ -142,6 +150,14 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   const void* ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  if (sparse) {
+    if (!mask) return FA_ERR_INVALID_ARG;
+    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    // the kernels list the kept rows of a mask column / columns of two mask rows in LDS
+    const size_t nb = ((size_t)N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+    if (bwd_dkdv_static_lds(d) + ((nb * 2 + 15) & ~(size_t)15) > kLdsBytes) return FA_ERR_UNSUPPORTED;
+    if (kBwdDqStaticLds + ((nb * 4 + 15) & ~(size_t)15) > kLdsBytes) return FA_ERR_UNSUPPORTED;
+  }
   const size_t need = fa_bwd_workspace_size(B, H, N, d, grad_dtype);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
@@ -156,6 +172,10 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
       if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
     for (int j = i + 1; j < 4; ++j)
       if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
+    if (sparse) {
+      const size_t nb = ((size_t)N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
+      if (overlap(outs[i], range_of(mask, nb * nb))) return FA_ERR_INVALID_ARG;
+    }
   }
   fa::BwdParams p;
   p.q = q;
@@ -176,8 +196,28 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
   p.causal = causal;
   p.dtype = dtype;
   p.grad_dtype = grad_dtype;
+  p.mask = sparse ? mask : nullptr;
   const hipError_t e = fa::launch_bwd(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+           void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype, int grad_dtype,
+           void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, nullptr, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, dtype, grad_dtype, workspace,
+                  workspace_bytes, stream, false);
+}
+
+int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const unsigned char* block_mask, const void* o,
+                       const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                       float scale, int causal, int dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  return bwd_impl(q, k, v, block_mask, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, dtype, grad_dtype,
+                  workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

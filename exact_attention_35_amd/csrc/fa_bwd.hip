@@ -117,6 +117,8 @@ struct BwdBf16Args {
   const unsigned short* v;
   const unsigned short* dO;
   const float2* stats;  // per row: (lse log2 e, D)
+  const unsigned char* mask;  // block-sparse 128x128 tile mask [nb, nb], or null
+  int nb;
   void* dq;
   void* dk;
   void* dv;
@@ -163,19 +165,27 @@ __device__ __forceinline__ void sched_dq_gemm() {
   for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
-template <int D, int BN, bool CAUSAL>
+// Block-sparse (SPARSE): as in the block-sparse forward, SIMDs 0-1 and 2-3 serve
+// the two 128-row mask rows of the workgroup's 256 queries, each walking its own
+// row's kept key tiles through its own half of every ring buffer.
+template <int D, int BN, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   using C = TileCfg<D, BN>;
   constexpr int BM = 256;
   constexpr int NSB = C::NSB;
   constexpr int NPT = C::NPT;
   constexpr int NDB = D / 32;
-  __shared__ __align__(16) unsigned short kbuf_0[C::TILE];
-  __shared__ __align__(16) unsigned short kbuf_1[C::TILE];
-  __shared__ __align__(16) unsigned short kbuf_2[C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_0[C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_1[C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_2[C::TILE];
+  constexpr int HT = SPARSE ? 2 : 1;            // independent tile streams
+  constexpr int NW = 4 / HT;                    // waves of a group that load one tile
+  constexpr int LPW = C::TILE * 2 / 1024 / NW;  // 1 KB loads per wave per tile
+  __shared__ __align__(16) unsigned short kbuf_0[HT * C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_1[HT * C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_2[HT * C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_0[HT * C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_1[HT * C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_2[HT * C::TILE];
+  extern __shared__ __align__(16) unsigned short col_list[];  // SPARSE: two lists of mask columns
+  __shared__ int list_len[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -198,9 +208,52 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   const int q_first = qt * BM;
   const int wave_q0 = q_first + 32 * (2 * wg + grp);
   const int qrow = wave_q0 + l32;
-  const int kend = CAUSAL ? min(N, q_first + BM) : N;
-  const int ntiles = (kend + BN - 1) / BN;
-  auto tile_at = [&](int t) __attribute__((always_inline)) -> int { return min(t, ntiles - 1); };
+  const int hs = SPARSE ? (wg >> 1) : 0;  // this wave's tile stream
+  const int wi = SPARSE ? (wg & 1) : wg;  // this wave's share of a tile load
+  unsigned short* const kb0 = kbuf_0 + hs * C::TILE;
+  unsigned short* const kb1 = kbuf_1 + hs * C::TILE;
+  unsigned short* const kb2 = kbuf_2 + hs * C::TILE;
+  unsigned short* const vb0 = vbuf_0 + hs * C::TILE;
+  unsigned short* const vb1 = vbuf_1 + hs * C::TILE;
+  unsigned short* const vb2 = vbuf_2 + hs * C::TILE;
+  int ntiles, nsteps;
+  if (SPARSE) {
+    constexpr int R = 128 / BN;  // key tiles per mask column
+    const int nb = a.nb;
+    if (w < 2) {  // wave h lists the columns kept by mask row 2 qt + h
+      const int r = 2 * qt + w;
+      const int ncol = r >= nb ? 0 : (CAUSAL ? r + 1 : nb);
+      const unsigned char* mrow = a.mask + (size_t)min(r, nb - 1) * nb;
+      int cnt = 0;
+      for (int base = 0; base < ncol; base += 64) {
+        const int col = base + lane;
+        const bool on = col < ncol && mrow[col] != 0;
+        const unsigned long long bal = __ballot(on);
+        if (on) col_list[w * nb + cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)col;
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) list_len[w] = cnt;
+    }
+    __syncthreads();
+    auto tiles_of = [&](int h) __attribute__((always_inline)) -> int {
+      const int len = list_len[h];
+      int n = len * R;
+      if (len > 0 && col_list[h * nb + len - 1] == nb - 1) n -= R - ((N - (nb - 1) * 128 + BN - 1) / BN);
+      return n;
+    };
+    ntiles = tiles_of(hs);
+    nsteps = max(tiles_of(0), tiles_of(1));
+  } else {
+    const int kend = CAUSAL ? min(N, q_first + BM) : N;
+    ntiles = (kend + BN - 1) / BN;
+    nsteps = ntiles;
+  }
+  auto tile_at = [&](int t) __attribute__((always_inline)) -> int {
+    const int tt = min(t, ntiles - 1);
+    if (!SPARSE) return tt;
+    constexpr int R = 128 / BN;
+    return (int)col_list[hs * a.nb + tt / R] * R + tt % R;
+  };
   auto need_mask = [&](int kt) __attribute__((always_inline)) -> bool {
     const int k_first = kt * BN;
     return (k_first + BN > N) || (CAUSAL && k_first + BN - 1 > wave_q0);
@@ -209,7 +262,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   // Every tile buffer starts as zeros: K(-1) is read (times dS = 0) by the first
   // MFMA phase, and rows past N (which the range-checked loads may leave
   // unwritten) are multiplied by zeros, so they must hold finite values.
-  for (int i = tid; i < C::TILE / 8; i += 512) {
+  for (int i = tid; i < HT * C::TILE / 8; i += 512) {
     reinterpret_cast<uint4*>(kbuf_0)[i] = zero_uint4();
     reinterpret_cast<uint4*>(kbuf_1)[i] = zero_uint4();
     reinterpret_cast<uint4*>(kbuf_2)[i] = zero_uint4();
@@ -218,14 +271,16 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
     reinterpret_cast<uint4*>(vbuf_2)[i] = zero_uint4();
   }
   barrier_lds();
-  if (grp == 1) {
-    dma_k<D, BN>(kres, kbuf_0, tile_at(0), wg, lane);
-    wait_dma();
-  } else {
-    dma_k<D, BN>(vres, vbuf_0, tile_at(0), wg, lane);
-    dma_k<D, BN>(vres, vbuf_1, tile_at(1), wg, lane);
+  if (ntiles > 0) {
+    if (grp == 1) {
+      dma_k<D, BN, NW>(kres, kb0, tile_at(0), wi, lane);
+      wait_dma();
+    } else {
+      dma_k<D, BN, NW>(vres, vb0, tile_at(0), wi, lane);
+      dma_k<D, BN, NW>(vres, vb1, tile_at(1), wi, lane);
+    }
   }
-  barrier_ring<C::KB_PER_WAVE>();  // V(1) may still be landing
+  barrier_ring<LPW>();  // V(1) may still be landing
 
   // ---- this lane's query: Q and dO rows as MFMA B fragments, lse and D
   bf16x8 qf[D / 16], dof[D / 16];
@@ -299,29 +354,34 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
 
   // Step t: buffers rotate with t mod 3.  kprev holds K(t-1), kcur K(t), vcur V(t);
   // group B fetches K(t+1) into knext, group A V(t+2) into vnext2.
+  // (a block-sparse stream that has run out of tiles only keeps the barriers)
   auto step = [&](int t, const unsigned short* kprev, const unsigned short* kcur, unsigned short* knext,
                   const unsigned short* vcur, unsigned short* vnext2) __attribute__((always_inline)) {
+    const bool active = ntiles > 0 && t <= ntiles;
     if (grp == 0) {
-      dma_k<D, BN>(vres, vnext2, tile_at(t + 2), wg, lane);
-      gemm_phase(kprev, kcur, vcur);
+      if (active) {
+        dma_k<D, BN, NW>(vres, vnext2, tile_at(t + 2), wi, lane);
+        gemm_phase(kprev, kcur, vcur);
+      }
     } else {
-      dma_k<D, BN>(kres, knext, tile_at(t + 1), wg, lane);
-      if (t >= 1) vector_phase(t - 1);
+      if (active) dma_k<D, BN, NW>(kres, knext, tile_at(t + 1), wi, lane);
+      if (t >= 1 && t - 1 < ntiles) vector_phase(t - 1);
     }
     barrier_plain();
     if (grp == 0) {
       if (t < ntiles) vector_phase(t);
-      wait_lgkm_vm<C::KB_PER_WAVE>();  // V(t+1) has landed
+      wait_lgkm_vm<LPW>();  // V(t+1) has landed
     } else {
-      gemm_phase(kprev, kcur, vcur);
+      if (active) gemm_phase(kprev, kcur, vcur);
       wait_lgkm_vm<0>();  // K(t+1) has landed
     }
     barrier_ring<15>();
   };
-  for (int t = 0; t <= ntiles; t += 3) {
-    step(t, kbuf_2, kbuf_0, kbuf_1, vbuf_0, vbuf_2);
-    if (t + 1 <= ntiles) step(t + 1, kbuf_0, kbuf_1, kbuf_2, vbuf_1, vbuf_0);
-    if (t + 2 <= ntiles) step(t + 2, kbuf_1, kbuf_2, kbuf_0, vbuf_2, vbuf_1);
+  // every wave runs the same steps (the barriers need it)
+  for (int t = 0; nsteps > 0 && t <= nsteps; t += 3) {
+    step(t, kb2, kb0, kb1, vb0, vb2);
+    if (t + 1 <= nsteps) step(t + 1, kb0, kb1, kb2, vb1, vb0);
+    if (t + 2 <= nsteps) step(t + 2, kb1, kb2, kb0, vb2, vb1);
   }
   wait_dma();  // no LDS-direct load may outlive the workgroup
 
@@ -379,7 +439,9 @@ struct DkvCfg : TileCfg<D, 64> {
   static constexpr int BQ = 64;   // queries per tile
 };
 
-template <int D, bool CAUSAL>
+// Block-sparse (SPARSE): the workgroup's 128 keys are one mask column; it visits
+// the 64-query tiles of the mask rows that keep that column.
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
   using C = DkvCfg<D>;
   constexpr int BQ = C::BQ;
@@ -396,6 +458,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
   __shared__ __align__(16) float2 st_1[BQ];
   __shared__ __align__(16) float2 st_2[BQ];
   __shared__ __align__(16) uint4 xch[4][2 * NPT][64];  // per SIMD: P then dS fragments, per lane
+  extern __shared__ __align__(16) unsigned short row_list[];  // SPARSE: mask rows that keep this column
+  __shared__ int row_len;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -417,11 +481,37 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
   const int mykey = wave_k0 + l32;
   const int nqt = (N + BQ - 1) / BQ;
   const int t_first = CAUSAL ? k0 / BQ : 0;
-  const int T = nqt - t_first;  // >= 1: k0 < N
+  int T;  // query tiles this workgroup visits
+  if (SPARSE) {
+    const int nb = a.nb;
+    if (w == 0) {
+      int cnt = 0;
+      for (int base = CAUSAL ? kt : 0; base < nb; base += 64) {
+        const int rb = base + lane;
+        const bool on = rb < nb && a.mask[(size_t)rb * nb + kt] != 0;
+        const unsigned long long bal = __ballot(on);
+        if (on) row_list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)rb;
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) row_len = cnt;
+    }
+    __syncthreads();
+    const int len = row_len;
+    T = 2 * len;  // two 64-query tiles per mask row, but none past N
+    if (len > 0 && row_list[len - 1] == nb - 1 && N <= (nb - 1) * 128 + BQ) T -= 1;
+  } else {
+    T = nqt - t_first;  // >= 1: k0 < N
+  }
+  // query tile of step i (steps past the list stay in range; their tiles are masked)
+  auto tile_q = [&](int i) __attribute__((always_inline)) -> int {
+    if (!SPARSE) return t_first + i;
+    const int j = min(i >> 1, max(row_len - 1, 0));
+    return (int)row_list[j] * 2 + (i & 1);
+  };
 
-  // tile i (queries (t_first + i) * 64 ..) into buffer set i % 3, by the gradient waves
+  // tile i into buffer set i % 3, by the gradient waves
   auto fetch = [&](int i, unsigned short* qb, unsigned short* ob, float2* st) __attribute__((always_inline)) {
-    const int tq = t_first + i;
+    const int tq = tile_q(i);
     dma_k<D, BQ>(qres, qb, tq, sw, lane);
     dma_k<D, BQ>(dores, ob, tq, sw, lane);
     if (sw == 0 && lane < 32)  // 64 rows x 8 bytes; rows past N read as zeros
@@ -442,7 +532,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
   }
   if (tid < BQ) st_0[tid] = st_1[tid] = st_2[tid] = make_float2(0.f, 0.f);
   barrier_lds();
-  if (!score) {
+  if (!score && T > 0) {
     fetch(0, qbuf_0, obuf_0, st_0);
     if (T > 1) {
       fetch(1, qbuf_1, obuf_1, st_1);
@@ -524,7 +614,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
       }
     };
     auto score_vector = [&](int i, const float2* st) __attribute__((always_inline)) {
-      const int q0 = (t_first + i) * BQ;
+      const int q0 = i < T ? tile_q(i) * BQ : N;  // past the last tile: everything masked
       if ((q0 + BQ > N) || (CAUSAL && q0 < wave_k0 + 31)) score_body(q0, st, std::true_type{});
       else score_body(q0, st, std::false_type{});
     };
@@ -750,7 +840,7 @@ static void launch_prep(const BwdParams& p, hipStream_t stream) {
                      static_cast<const T*>(p.dO), p.lse, reinterpret_cast<float2*>(p.stats), rows);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   BwdBf16Args a;
   a.q = static_cast<const unsigned short*>(p.q);
@@ -767,11 +857,23 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   a.c = fmaxf(fabsf(p.scale) * kLog2e, 0x1p-100f);
   a.scale = p.scale;
   a.neg = p.scale < 0.f ? 1 : 0;
-  const unsigned nkb = (unsigned)((p.N + 127) / 128);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(nkb * (unsigned)a.BH), dim3(512), 0, stream, a);
+  a.mask = p.mask;
+  a.nb = (p.N + 127) / 128;
+  // block-sparse: the mask-row / mask-column lists live in dynamic LDS
+  const size_t dyn_kv = SPARSE ? (((size_t)a.nb * 2 + 15) & ~(size_t)15) : 0;
+  const size_t dyn_q = SPARSE ? (((size_t)a.nb * 4 + 15) & ~(size_t)15) : 0;
+  constexpr int DQ_BN = D == 128 ? 32 : 64;  // keys per dQ tile (8 KB): keeps the d = 128 kernel within 256 VGPRs
+  if (SPARSE) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, SPARSE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_kv);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel<D, DQ_BN, CAUSAL, SPARSE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_q);
+  }
+  const unsigned nkb = (unsigned)a.nb;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(nkb * (unsigned)a.BH), dim3(512), dyn_kv, stream, a);
   const unsigned nqb = (unsigned)((p.N + 255) / 256);
-  constexpr int DQ_BN = D == 128 ? 32 : 64;  // keys per dQ tile: keeps the d = 128 kernel within 256 VGPRs
-  hipLaunchKernelGGL((bwd_dq_kernel<D, DQ_BN, CAUSAL>), dim3(nqb * (unsigned)a.BH), dim3(512), 0, stream, a);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, DQ_BN, CAUSAL, SPARSE>), dim3(nqb * (unsigned)a.BH), dim3(512), dyn_q, stream,
+                     a);
 }
 
 template <int D, bool CAUSAL>
@@ -806,12 +908,22 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
     }
     return hipGetLastError();
   }
+  const bool sparse = p.mask != nullptr;
   if (p.d == 64) {
     launch_prep<unsigned short, 64>(p, stream);
-    if (p.causal) launch_bwd_bf16<64, true>(p, stream); else launch_bwd_bf16<64, false>(p, stream);
+    if (sparse) {
+      if (p.causal) launch_bwd_bf16<64, true, true>(p, stream); else launch_bwd_bf16<64, false, true>(p, stream);
+    } else {
+      if (p.causal) launch_bwd_bf16<64, true, false>(p, stream); else launch_bwd_bf16<64, false, false>(p, stream);
+    }
   } else {
     launch_prep<unsigned short, 128>(p, stream);
-    if (p.causal) launch_bwd_bf16<128, true>(p, stream); else launch_bwd_bf16<128, false>(p, stream);
+    if (sparse) {
+      if (p.causal) launch_bwd_bf16<128, true, true>(p, stream); else launch_bwd_bf16<128, false, true>(p, stream);
+    } else {
+      if (p.causal) launch_bwd_bf16<128, true, false>(p, stream);
+      else launch_bwd_bf16<128, false, false>(p, stream);
+    }
   }
   return hipGetLastError();
 }

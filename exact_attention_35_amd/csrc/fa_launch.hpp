@@ -31,6 +31,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* stats;  // workspace: per row of [B, H, N], the pair (lse * log2 e, D = rowsum(dO * O))
+  const unsigned char* mask;  // block-sparse tile mask (bf16 only), null when dense
   int B, H, N, d;
   float scale;
   int causal;

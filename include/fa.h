@@ -105,6 +105,21 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
            int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Block-sparse backward.  Gradients of L = sum(dO * O) for the block-sparse
+ * attention of fa_fwd_blocksparse (same block_mask, scale and causal; o and lse
+ * from that call).  Masked 128x128 tiles cost neither HBM traffic nor MFMA
+ * work: the dK/dV pass visits, per 128-key block, the query tiles of the mask
+ * rows that keep its column, the dQ pass the key tiles of each query row's
+ * kept columns.  bf16 inputs only; arguments, workspace and errors as fa_bwd.
+ * Block-sparse training is part of the FlashAttention abstract's block-sparse
+ * extension (scite.ai page of Tri Dao).
+ */
+int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const unsigned char* block_mask,
+                       const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                       int B, int H, int N, int d, float scale, int causal, int dtype, int grad_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* fa_status_string(int status);
 

@@ -86,6 +86,19 @@ def test_blocksparse_validation(lib):
         assert f(*base, P + 5 * MB, P + 3 * MB, P + 4 * MB, 1, 1, n_bad, d, 0.125, 1, 1, None) == UNS
 
 
+def test_blocksparse_backward_validation(lib):
+    f = lib.fa_bwd_blocksparse
+    ptrs = [P + i * MB for i in range(10)]
+    ws_bytes = lib.fa_bwd_workspace_size(1, 2, 64, 64, 0)
+    def call(mask=ptrs[3], dtype=1, d=64, n=64):
+        return f(ptrs[0], ptrs[1], ptrs[2], mask, ptrs[4], ptrs[5], ptrs[6], ptrs[7], ptrs[8], ptrs[9],
+                 1, 2, n, d, 0.125, 1, dtype, 0, P + 11 * MB, ws_bytes, None)
+    assert call(mask=None) == INV
+    assert call(dtype=0) == UNS  # fp32 block-sparse
+    assert call(d=96) == UNS
+    assert call(mask=ptrs[7]) == INV  # the mask overlaps an output
+
+
 def test_head_slice_limit(lib):
     # one head's [N, d] slice is addressed with 32-bit byte offsets
     ptrs = (P, P + MB, P + 2 * MB, P + 3 * MB, P + 4 * MB)

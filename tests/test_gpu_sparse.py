@@ -75,3 +75,47 @@ def test_full_masks_equal_dense(d):
         for oo, ll in ((os_, ls_), (host(o), host(lse))):
             assert max_err(oo, ro) <= TOL_BF16 and max_err(ll, rl) <= TOL_LSE, (d, causal)
         assert max_err(os_, host(o)) <= TOL_BF16 and max_err(ls_, host(lse)) <= TOL_LSE, (d, causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_backward(d, causal):
+    """fa_bwd_blocksparse against the oracle's gradients of the masked attention."""
+    for n in (100, 129, 500, 1030):
+        nb = -(-n // 128)
+        announce(f"sparse bwd N={n} d={d} causal={causal}")
+        # N(0, 1) activations as in the workloads: with sharper logits the bf16 rounding of
+        # P and dS alone approaches the 2e-2 bound (as it does for the dense backward)
+        q, k, v, do = inputs.random_case(23, 1, 2, n, d, "bf16", backward=True)
+        mask = inputs.random_block_mask(24, nb, 0.4, causal)
+        if nb > 2:
+            mask[1, :] = 0  # a mask row with no visible key: its dQ is 0
+        if nb > 3:
+            mask[:, 2] = 0  # a mask column no query sees: its dK, dV are 0
+        scale = api.default_scale(d)
+        tm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda:0")
+        tq, tk, tv, tdo = dev(q, BF), dev(k, BF), dev(v, BF), dev(do, BF)
+        o, lse = api.forward_blocksparse(tq, tk, tv, tm, scale, causal)
+        dq, dk, dv = api.backward(tq, tk, tv, o, lse, tdo, scale, causal, block_mask=tm)
+        torch.cuda.synchronize()
+        rq, rk, rv = oracle.backward(q, k, v, do, scale, causal, mask, inputs.MASK_BLOCK)
+        eq, ek, ev = max_err(host(dq), rq), max_err(host(dk), rk), max_err(host(dv), rv)
+        report(f"sparse bwd N={n} d={d} causal={causal}", dq=eq, dk=ek, dv=ev)
+        assert eq <= TOL_BF16 and ek <= TOL_BF16 and ev <= TOL_BF16, (n, d, causal)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_blocksparse_backward_full_mask_equals_dense(d):
+    n = 600
+    nb = -(-n // 128)
+    announce(f"sparse bwd == dense d={d}")
+    q, k, v, do = inputs.random_case(25, 1, 2, n, d, "bf16", backward=True)
+    tq, tk, tv, tdo = dev(q, BF), dev(k, BF), dev(v, BF), dev(do, BF)
+    for causal in (False, True):
+        tm = torch.ones((nb, nb), dtype=torch.uint8, device="cuda:0")
+        o, lse = api.forward(tq, tk, tv, 0.1, causal)
+        sparse = api.backward(tq, tk, tv, o, lse, tdo, 0.1, causal, block_mask=tm)
+        dense = api.backward(tq, tk, tv, o, lse, tdo, 0.1, causal)
+        torch.cuda.synchronize()
+        for a_, b_ in zip(sparse, dense):
+            assert max_err(host(a_), host(b_)) <= TOL_BF16, (d, causal)
