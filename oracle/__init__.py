@@ -20,6 +20,8 @@ Parity status of each function (how it is pinned, in tests/test_oracle_*.py):
   forward / forward_rows      -- brute force, closed forms, torch fp64 SDPA, golden hand cases
   forward_blockwise / merge   -- equals the one-shot forward; the dropped-l mutation fails
   backward                    -- central finite differences, torch fp64 autograd, invariants
+  grouped-/multi-query heads  -- torch fp64 SDPA and autograd with enable_gqa, brute force and
+                                 finite differences, K/V heads repeated == plain multi-head
 """
 
 from .attention import (  # noqa: F401
@@ -28,6 +30,7 @@ from .attention import (  # noqa: F401
     forward,
     forward_blockwise,
     forward_rows,
+    kv_head,
     merge_partials,
     probabilities,
 )

@@ -5,7 +5,13 @@ independent of the HIP library.
 
 Layout of every tensor argument: [B, H, N, d] (d innermost), any float dtype;
 values are upcast exactly to float64 before any arithmetic.  Results are
-float64.  `lse` is [B, H, N], natural log.
+float64.  `lse` is [B, H, N], natural log.  K and V (and dK, dV) may carry
+fewer heads, H_kv, than Q: grouped-query attention, or multi-query attention
+when H_kv = 1 (everydayai.blog flash-attention article, "FlashAttention-2",
+point 3, names both variants without defining them).  Reading used: H_kv
+divides H and query head h reads key/value head h // (H / H_kv), so each run
+of H / H_kv consecutive query heads shares one K/V head; dK and dV of a shared
+head are the sums over its query heads (the chain rule through the sharing).
 
 Definition followed (everydayai.blog flash-attention article, opening
 ``standard_attention`` snippet, and "The Math Behind Flash Attention",
@@ -33,6 +39,13 @@ import numpy as np
 
 def _f64(x):
     return np.asarray(x, dtype=np.float64)
+
+
+def kv_head(h, n_heads, n_kv_heads):
+    """Key/value head read by query head h (grouped-query reading in the header)."""
+    if n_kv_heads < 1 or n_heads % n_kv_heads != 0:
+        raise ValueError(f"{n_heads} query heads cannot share {n_kv_heads} key/value heads evenly")
+    return h // (n_heads // n_kv_heads)
 
 
 def allowed(rows, n_keys, causal, block_mask=None, mask_block=128, cols=None):
@@ -100,9 +113,10 @@ def forward_rows(q, k, v, rows, scale, causal=False, block_mask=None, mask_block
         groups = [np.nonzero(chunk == c)[0] for c in np.unique(chunk)]
     for b in range(B):
         for h in range(H):
+            kh = kv_head(h, H, k.shape[1])
             for g in groups:
                 o[b, h, g], lse[b, h, g] = _rows_one_head(
-                    q[b, h, rows[g]], k[b, h], v[b, h], rows[g], scale, causal, block_mask, mask_block)
+                    q[b, h, rows[g]], k[b, kh], v[b, kh], rows[g], scale, causal, block_mask, mask_block)
     return o, lse
 
 
@@ -131,7 +145,7 @@ def probabilities(q, k, scale, causal=False, block_mask=None, mask_block=128):
     p = np.zeros((B, H, N, N))
     for b in range(B):
         for h in range(H):
-            p[b, h] = _probs_one_head(q[b, h], k[b, h], ok, scale)
+            p[b, h] = _probs_one_head(q[b, h], k[b, kv_head(h, H, k.shape[1])], ok, scale)
     return p
 
 
@@ -182,14 +196,15 @@ def forward_blockwise(q, k, v, scale, causal=False, block_mask=None, mask_block=
     lse_all = np.full((B, H, N), -np.inf)
     for b in range(B):
         for h in range(H):
+            kh = kv_head(h, H, k.shape[1])
             m = np.full(N, -np.inf)
             l = np.zeros(N)
             o = np.zeros((N, v.shape[-1]))
             for j0 in range(0, N, block):
                 cols = np.arange(j0, min(j0 + block, N))
                 ok = allowed(rows, N, causal, block_mask, mask_block, cols=cols)
-                s = np.where(ok, scale * (q[b, h] @ k[b, h, cols].T), -np.inf)
-                m, l, o = merge_block(m, l, o, s, v[b, h, cols])
+                s = np.where(ok, scale * (q[b, h] @ k[b, kh, cols].T), -np.inf)
+                m, l, o = merge_block(m, l, o, s, v[b, kh, cols])
             has = np.isfinite(m)
             o_all[b, h] = o
             lse_all[b, h, has] = m[has] + np.log(l[has])
@@ -225,7 +240,7 @@ def merge_partials(lse_x, o_x, lse_y, o_y):
 # ---------------------------------------------------------------------------
 
 def backward(q, k, v, do, scale, causal=False, block_mask=None, mask_block=128, return_delta=False):
-    """(dq, dk, dv) in float64, each [B, H, N, d]; optionally also D [B, H, N]."""
+    """(dq [B, H, N, d], dk and dv [B, H_kv, N, d]) in float64; optionally also D [B, H, N]."""
     q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
     N = q.shape[2]
     ok = allowed(np.arange(N), N, causal, block_mask, mask_block)
@@ -236,13 +251,14 @@ def backward(q, k, v, do, scale, causal=False, block_mask=None, mask_block=128, 
     B, H = q.shape[:2]
     for b in range(B):
         for h in range(H):
-            P = _probs_one_head(q[b, h], k[b, h], ok, scale)
-            dv[b, h] = P.T @ do[b, h]
-            dP = do[b, h] @ v[b, h].T
+            kh = kv_head(h, H, k.shape[1])
+            P = _probs_one_head(q[b, h], k[b, kh], ok, scale)
+            dv[b, kh] += P.T @ do[b, h]
+            dP = do[b, h] @ v[b, kh].T
             D = (P * dP).sum(axis=1)
             dS = P * (dP - D[:, None])
-            dq[b, h] = scale * (dS @ k[b, h])
-            dk[b, h] = scale * (dS.T @ q[b, h])
+            dq[b, h] = scale * (dS @ k[b, kh])
+            dk[b, kh] += scale * (dS.T @ q[b, h])
             delta[b, h] = D
     if return_delta:
         return dq, dk, dv, delta

@@ -34,11 +34,13 @@ def brute_forward(q, k, v, scale, causal=False, block_mask=None, mask_block=128)
     o = np.zeros((B, H, N, dv))
     lse = np.full((B, H, N), -math.inf)
     bm = None if block_mask is None else np.asarray(block_mask).tolist()
+    Hkv = k.shape[1]
     for b in range(B):
         for h in range(H):
+            # grouped-query sharing: query head h reads key/value head floor(h * H_kv / H)
             Q = q[b, h].tolist()
-            K = k[b, h].tolist()
-            V = v[b, h].tolist()
+            K = k[b, h * Hkv // H].tolist()
+            V = v[b, h * Hkv // H].tolist()
             for i in range(N):
                 w = {}
                 for j in range(N):

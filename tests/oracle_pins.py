@@ -269,6 +269,32 @@ def check_golden_forward():
         assert np.max(np.abs(lse[0, 0] - np.asarray(_eval(g[mode]["lse"])))) <= 1e-13
 
 
+def check_gqa_forward(seed=13):
+    """Grouped-/multi-query forward == torch fp64 SDPA with enable_gqa, == brute force, == K/V heads repeated."""
+    import torch
+
+    for hkv in (1, 2, 3, 6):
+        for causal in (False, True):
+            q = _rand(seed, (2, 6, 21, 5), 2.0)
+            k = _rand(seed + 1, (2, hkv, 21, 5), 2.0)
+            v = _rand(seed + 2, (2, hkv, 21, 5))
+            o, lse = oracle.forward(q, k, v, 0.45, causal)
+            tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                tq, tk, tv, is_causal=causal, scale=0.45, enable_gqa=True)
+            assert np.max(np.abs(o - ref.numpy())) <= 1e-12, (hkv, causal)
+            # each K/V head repeated for its run of consecutive query heads: plain multi-head attention
+            rk, rv = np.repeat(k, 6 // hkv, axis=1), np.repeat(v, 6 // hkv, axis=1)
+            o2, lse2 = oracle.forward(q, rk, rv, 0.45, causal)
+            assert np.max(np.abs(o - o2)) <= 1e-13 and np.max(np.abs(lse - lse2)) <= 1e-13
+    q, k, v = _rand(seed + 3, (1, 4, 6, 3)), _rand(seed + 4, (1, 2, 6, 3)), _rand(seed + 5, (1, 2, 6, 3))
+    bm = np.array([[1, 0, 0], [1, 1, 0], [0, 1, 1]], dtype=np.uint8)
+    for causal, mask in ((False, None), (True, None), (True, bm)):
+        o, lse = oracle.forward(q, k, v, 0.8, causal, mask, 2)
+        ob, lseb = oracle.brute_forward(q, k, v, 0.8, causal, mask, 2)
+        assert np.max(np.abs(o - ob)) <= 1e-13 and np.max(np.abs(lse - lseb)) <= 1e-13
+
+
 FORWARD_CHECKS = [
     check_brute_force,
     check_rows_sum_to_one,
@@ -281,6 +307,7 @@ FORWARD_CHECKS = [
     check_merge_partials,
     check_torch_sdpa,
     check_golden_forward,
+    check_gqa_forward,
 ]
 
 
@@ -352,11 +379,50 @@ def check_golden_backward():
             assert np.max(np.abs(got[0, 0] - np.asarray(_eval(g[mode][name])))) <= 1e-13, (mode, name)
 
 
+def check_gqa_backward(seed=14):
+    """Grouped-/multi-query gradients == central finite differences, == torch fp64 autograd with enable_gqa.
+
+    dK and dV of a shared head must be the sums over its query heads: with K/V
+    heads repeated per query head (plain multi-head attention), the group sums of
+    the per-head gradients.
+    """
+    import torch
+
+    for hkv, shp in ((1, (1, 3, 4, 2)), (2, (1, 4, 5, 2))):
+        for causal in (False, True):
+            q = _rand(seed, shp)
+            k = _rand(seed + 1, (shp[0], hkv) + shp[2:])
+            v = _rand(seed + 2, (shp[0], hkv) + shp[2:])
+            do = _rand(seed + 3, shp)
+            got = oracle.backward(q, k, v, do, 0.7, causal)
+            fd = oracle.brute_backward_fd(q, k, v, do, 0.7, causal)
+            for g, f in zip(got, fd):
+                assert g.shape == f.shape
+                assert np.max(np.abs(g - f)) / max(1.0, np.max(np.abs(f))) <= 1e-6, (hkv, causal)
+    for hkv in (1, 2, 4):
+        for causal in (False, True):
+            q, do = _rand(seed + 10, (2, 4, 19, 6)), _rand(seed + 11, (2, 4, 19, 6))
+            k, v = _rand(seed + 12, (2, hkv, 19, 6)), _rand(seed + 13, (2, hkv, 19, 6))
+            tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+            out = torch.nn.functional.scaled_dot_product_attention(
+                tq, tk, tv, is_causal=causal, scale=0.4, enable_gqa=True)
+            (out * torch.from_numpy(do)).sum().backward()
+            got = oracle.backward(q, k, v, do, 0.4, causal)
+            for g, t in zip(got, (tq.grad, tk.grad, tv.grad)):
+                assert np.max(np.abs(g - t.numpy())) <= 1e-12, (hkv, causal)
+            g = 4 // hkv
+            rq = oracle.backward(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), do, 0.4, causal)
+            assert np.max(np.abs(got[0] - rq[0])) <= 1e-13
+            for a, r in ((got[1], rq[1]), (got[2], rq[2])):
+                assert np.max(np.abs(a - r.reshape(2, hkv, g, 19, 6).sum(axis=2))) <= 1e-12
+
+
 BACKWARD_CHECKS = [
     check_finite_differences,
     check_torch_autograd,
     check_backward_invariants,
     check_golden_backward,
+    check_gqa_backward,
 ]
 
 ALL_CHECKS = FORWARD_CHECKS + BACKWARD_CHECKS

@@ -89,12 +89,30 @@ def _backward_delta_dropped(q, k, v, do, scale, causal=False, block_mask=None, m
     D = np.zeros(q64.shape[:3])
     for b in range(q64.shape[0]):
         for h in range(q64.shape[1]):
-            P = oatt._probs_one_head(q64[b, h], k64[b, h], ok, scale)
-            dv[b, h] = P.T @ do64[b, h]
-            dS = P * (do64[b, h] @ v64[b, h].T)  # the "- D" term dropped
-            dq[b, h] = scale * dS @ k64[b, h]
-            dk[b, h] = scale * dS.T @ q64[b, h]
+            kh = oatt.kv_head(h, q64.shape[1], k64.shape[1])
+            P = oatt._probs_one_head(q64[b, h], k64[b, kh], ok, scale)
+            dv[b, kh] += P.T @ do64[b, h]
+            dS = P * (do64[b, h] @ v64[b, kh].T)  # the "- D" term dropped
+            dq[b, h] = scale * dS @ k64[b, kh]
+            dk[b, kh] += scale * dS.T @ q64[b, h]
     return (dq, dk, dv, D) if return_delta else (dq, dk, dv)
+
+
+def _kv_head_interleaved(h, n_heads, n_kv_heads):
+    return h % n_kv_heads  # query heads dealt round-robin instead of in consecutive runs
+
+
+def _backward_group_not_summed(q, k, v, do, scale, causal=False, block_mask=None, mask_block=128,
+                               return_delta=False):
+    """dK/dV of a shared K/V head taken from the last query head of its group only (assigned, not added)."""
+    B, H, N, d = np.shape(q)
+    hkv = np.shape(k)[1]
+    g = H // hkv
+    out = list(_orig_backward(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), do, scale, causal,
+                              block_mask, mask_block, True))
+    out[1] = out[1].reshape(B, hkv, g, N, d)[:, :, -1]
+    out[2] = out[2].reshape(B, hkv, g, N, d)[:, :, -1]
+    return tuple(out) if return_delta else tuple(out[:3])
 
 
 _orig_backward = oatt.backward
@@ -110,6 +128,8 @@ MUTATIONS = {
     "probs_not_normalised": ("_probs_one_head", _probs_row_sum_off, pins.ALL_CHECKS),
     "dk_sign": ("backward", _backward_sign_flip, pins.BACKWARD_CHECKS),
     "delta_dropped": ("backward", _backward_delta_dropped, pins.BACKWARD_CHECKS),
+    "kv_heads_interleaved": ("kv_head", _kv_head_interleaved, pins.ALL_CHECKS),
+    "gqa_grads_not_summed": ("backward", _backward_group_not_summed, pins.BACKWARD_CHECKS),
 }
 
 
