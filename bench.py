@@ -100,6 +100,8 @@ def kernel_table():
         tq, tk, tv = to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16)
         del q, k, v
         entry = {"shape": list(w.shape), "causal": w.causal}
+        if w.Hkv is not None:
+            entry["kv_heads"] = w.kv_heads
         if w.sparse:
             nb = -(-w.N // inputs.MASK_BLOCK)
             mask = inputs.make_block_mask(nb, w.density, w.index, causal=w.causal)
@@ -118,10 +120,11 @@ def kernel_table():
         else:
             ms = time_calls(lambda: api.forward(tq, tk, tv, w.scale, w.causal), 20)
             entry.update(fwd_ms=ms, fwd_tflops=flops_fwd(w) / ms / 1e9)
-            if w.backward or w.name == "long_s16k_d128":
+            if w.backward or w.name == "long_s16k_d128" or w.Hkv is not None:
                 o, lse = api.forward(tq, tk, tv, w.scale, w.causal)
                 tdo = to_dev(inputs.draw(w.index, inputs.SLOT_DO, w.shape), torch.bfloat16)
-                ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda:0")
+                ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d, H_kv=w.kv_heads), dtype=torch.uint8,
+                                 device="cuda:0")
                 bms = time_calls(lambda: api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws), 10)
                 entry.update(bwd_ms=bms, bwd_tflops=2.5 * flops_fwd(w) / bms / 1e9)
         entry["fwd_frac_peak"] = entry["fwd_tflops"] / PEAK_BF16_TFLOPS

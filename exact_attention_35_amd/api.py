@@ -2,7 +2,9 @@
 
 PyTorch supplies device memory and the current HIP stream; every step of the
 computation runs in the library's HIP kernels.  Tensors are [B, H, N, d],
-contiguous, on one GPU, bfloat16 or float32.
+contiguous, on one GPU, bfloat16 or float32.  K and V may carry H_kv < H heads
+(grouped-query; H_kv = 1 is multi-query): query head h then reads K/V head
+h // (H // H_kv), and the dense entry points route to fa_fwd_gqa / fa_bwd_gqa.
 """
 
 from __future__ import annotations
@@ -20,11 +22,15 @@ def _stream_ptr(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
-    if q.dim() != 4:
+def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, allow_gqa: bool = False):
+    """(B, H, N, d) of q, plus checks; with allow_gqa, k and v may be [B, H_kv, N, d], H_kv | H."""
+    if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q, k, v must be [B, H, N, d]")
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    B, H, N, d = q.shape
+    hkv = k.shape[1]
+    gqa_ok = allow_gqa and hkv >= 1 and H % hkv == 0
+    if v.shape != k.shape or k.shape != (B, hkv if gqa_ok else H, N, d):
+        raise ValueError(f"q, k, v shapes do not fit: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype bfloat16 or float32")
     for t in (q, k, v):
@@ -44,18 +50,27 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[f
             causal: bool = False, with_lse: bool = True,
             out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None
             ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Exact attention forward: returns (o, lse), lse fp32 [B, H, N] (None if with_lse=False)."""
-    B, H, N, d = _check_qkv(q, k, v)
+    """Exact attention forward: returns (o, lse), lse fp32 [B, H, N] (None if with_lse=False).
+
+    k and v may hold fewer heads than q (grouped-/multi-query, fa_fwd_gqa).
+    """
+    B, H, N, d = _check_qkv(q, k, v, allow_gqa=True)
+    hkv = k.shape[1]
     scale = default_scale(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     lse = None
     if with_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    lib = _lib.load()
+    lse_ptr = lse.data_ptr() if lse is not None else None
     with torch.cuda.device(q.device):
-        st = _lib.load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                lse.data_ptr() if lse is not None else None, B, H, N, d, scale,
-                                int(bool(causal)), _DTYPES[q.dtype], _stream_ptr(q.device))
-    _lib.check(st, "fa_fwd")
+        if hkv == H:
+            st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_ptr, B, H, N, d, scale,
+                            int(bool(causal)), _DTYPES[q.dtype], _stream_ptr(q.device))
+        else:
+            st = lib.fa_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_ptr, B, H, hkv, N, d,
+                                scale, int(bool(causal)), _DTYPES[q.dtype], _stream_ptr(q.device))
+    _lib.check(st, "fa_fwd" if hkv == H else "fa_fwd_gqa")
     return o, lse
 
 
@@ -84,8 +99,11 @@ def forward_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
     return o, lse
 
 
-def bwd_workspace_size(B: int, H: int, N: int, d: int, grad_dtype: torch.dtype = torch.float32) -> int:
-    return int(_lib.load().fa_bwd_workspace_size(B, H, N, d, _DTYPES[grad_dtype]))
+def bwd_workspace_size(B: int, H: int, N: int, d: int, grad_dtype: torch.dtype = torch.float32,
+                       H_kv: Optional[int] = None) -> int:
+    if H_kv is None or H_kv == H:
+        return int(_lib.load().fa_bwd_workspace_size(B, H, N, d, _DTYPES[grad_dtype]))
+    return int(_lib.load().fa_bwd_gqa_workspace_size(B, H, H_kv, N, d, _DTYPES[grad_dtype]))
 
 
 def _check_mask(block_mask: torch.Tensor, N: int, device: torch.device) -> None:
@@ -103,9 +121,11 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     """Gradients (dq, dk, dv) of sum(do * o), in grad_dtype (float32 by default).
 
     With block_mask (uint8 [ceil(N/128), ceil(N/128)], as for forward_blocksparse) this is
-    the block-sparse backward, fa_bwd_blocksparse.
+    the block-sparse backward, fa_bwd_blocksparse.  With k and v of H_kv < H heads it is the
+    grouped-query backward, fa_bwd_gqa: dk and dv then have k's shape.
     """
-    B, H, N, d = _check_qkv(q, k, v)
+    B, H, N, d = _check_qkv(q, k, v, allow_gqa=block_mask is None)
+    hkv = k.shape[1]
     if block_mask is not None:
         _check_mask(block_mask, N, q.device)
     for name, t in (("o", o), ("do", do)):
@@ -117,23 +137,27 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         raise ValueError("grad_dtype must be torch.float32 or torch.bfloat16")
     scale = default_scale(d) if scale is None else float(scale)
     dq = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
-    dk = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
-    dv = torch.empty(q.shape, dtype=grad_dtype, device=q.device)
-    need = bwd_workspace_size(B, H, N, d, grad_dtype)
+    dk = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+    dv = torch.empty(k.shape, dtype=grad_dtype, device=q.device)
+    need = bwd_workspace_size(B, H, N, d, grad_dtype, hkv)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     lib = _lib.load()
-    tail = (B, H, N, d, scale, int(bool(causal)), _DTYPES[q.dtype], _DTYPES[grad_dtype], workspace.data_ptr(),
+    tail = (N, d, scale, int(bool(causal)), _DTYPES[q.dtype], _DTYPES[grad_dtype], workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
     with torch.cuda.device(q.device):
-        if block_mask is None:
-            st = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), *tail)
+        if block_mask is not None:
+            name = "fa_bwd_blocksparse"
+            st = lib.fa_bwd_blocksparse(*ptrs[:3], block_mask.data_ptr(), *ptrs[3:], B, H, *tail)
+        elif hkv != H:
+            name = "fa_bwd_gqa"
+            st = lib.fa_bwd_gqa(*ptrs, B, H, hkv, *tail)
         else:
-            st = lib.fa_bwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), block_mask.data_ptr(),
-                                        o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                                        dv.data_ptr(), *tail)
-    _lib.check(st, "fa_bwd" if block_mask is None else "fa_bwd_blocksparse")
+            name = "fa_bwd"
+            st = lib.fa_bwd(*ptrs, B, H, *tail)
+    _lib.check(st, name)
     return dq, dk, dv
 
 
@@ -156,5 +180,5 @@ class FlashAttentionFunction(torch.autograd.Function):
 
 
 def attention(q, k, v, scale=None, causal=False):
-    """Differentiable exact attention (bf16 gradients for bf16 inputs)."""
+    """Differentiable exact attention (bf16 gradients for bf16 inputs); k, v may have H_kv | H heads."""
     return FlashAttentionFunction.apply(q, k, v, scale, causal)

@@ -46,17 +46,22 @@ int check_common(int B, int H, int N, int d, float scale, int causal, int dtype)
 
 size_t elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
 
+// grouped-query: H_kv K/V heads, each shared by H / H_kv consecutive query heads
+bool valid_kv_heads(int H, int Hkv) { return Hkv >= 1 && Hkv <= H && H % Hkv == 0; }
+
 int fwd_impl(const void* q, const void* k, const void* v, const unsigned char* mask, void* o, float* lse,
-             int B, int H, int N, int d, float scale, int causal, int dtype, void* stream, bool sparse) {
+             int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype, void* stream, bool sparse) {
   int st = check_common(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
+  if (!valid_kv_heads(H, Hkv)) return FA_ERR_INVALID_ARG;
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (sparse && !mask) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return FA_ERR_INVALID_ARG;
   const size_t n = (size_t)B * H * N;
   const size_t tb = n * d * elem_bytes(dtype);
-  const Range in[3] = {range_of(q, tb), range_of(k, tb), range_of(v, tb)};
+  const size_t kvb = (size_t)B * Hkv * N * d * elem_bytes(dtype);
+  const Range in[3] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb)};
   const Range ro = range_of(o, tb);
   for (const Range& r : in) {
     if (overlap(ro, r)) return FA_ERR_INVALID_ARG;
@@ -81,6 +86,7 @@ int fwd_impl(const void* q, const void* k, const void* v, const unsigned char* m
   p.mask = sparse ? mask : nullptr;
   p.B = B;
   p.H = H;
+  p.Hkv = Hkv;
   p.N = N;
   p.d = d;
   p.scale = scale;
@@ -117,18 +123,29 @@ const char* fa_status_string(int status) {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
            float scale, int causal, int dtype, void* stream) {
-  return fwd_impl(q, k, v, nullptr, o, lse, B, H, N, d, scale, causal, dtype, stream, false);
+  return fwd_impl(q, k, v, nullptr, o, lse, B, H, H, N, d, scale, causal, dtype, stream, false);
+}
+
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
+               int d, float scale, int causal, int dtype, void* stream) {
+  return fwd_impl(q, k, v, nullptr, o, lse, B, H, H_kv, N, d, scale, causal, dtype, stream, false);
 }
 
 int fa_fwd_blocksparse(const void* q, const void* k, const void* v, const unsigned char* block_mask, void* o,
                        float* lse, int B, int H, int N, int d, float scale, int causal, int dtype, void* stream) {
-  return fwd_impl(q, k, v, block_mask, o, lse, B, H, N, d, scale, causal, dtype, stream, true);
+  return fwd_impl(q, k, v, block_mask, o, lse, B, H, H, N, d, scale, causal, dtype, stream, true);
+}
+
+size_t fa_bwd_gqa_workspace_size(int B, int H, int H_kv, int N, int d, int grad_dtype) {
+  if (check_common(B, H, N, d, 1.0f, 0, grad_dtype) != FA_OK || !valid_kv_heads(H, H_kv)) return 0;
+  const size_t n = (size_t)B * H * N;
+  size_t bytes = n * 8;  // per row: (lse * log2 e, D), two fp32
+  if (H_kv < H) bytes = ((bytes + 255) & ~(size_t)255) + 2 * n * d * 4;  // fp32 dK, dV per query head
+  return bytes;
 }
 
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int grad_dtype) {
-  if (check_common(B, H, N, d, 1.0f, 0, grad_dtype) != FA_OK) return 0;
-  const size_t n = (size_t)B * H * N;
-  return n * 8;  // per row: (lse * log2 e, D), two fp32
+  return fa_bwd_gqa_workspace_size(B, H, H, N, d, grad_dtype);
 }
 
 }  // extern "C"
@@ -140,10 +157,12 @@ constexpr size_t bwd_dkdv_static_lds(int d) { return d == 128 ? 132608 + 64 : 83
 constexpr size_t kBwdDqStaticLds = (size_t)6 * 16384 + 64;
 
 int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* mask, const void* o, const float* lse,
-             const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
-             int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream, bool sparse) {
+             const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale,
+             int causal, int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream,
+             bool sparse) {
   int st = check_common(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
+  if (!valid_kv_heads(H, Hkv)) return FA_ERR_INVALID_ARG;
   if (grad_dtype != FA_F32 && grad_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (dtype == FA_F32 && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
@@ -158,15 +177,18 @@ int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* m
     if (bwd_dkdv_static_lds(d) + ((nb * 2 + 15) & ~(size_t)15) > kLdsBytes) return FA_ERR_UNSUPPORTED;
     if (kBwdDqStaticLds + ((nb * 4 + 15) & ~(size_t)15) > kLdsBytes) return FA_ERR_UNSUPPORTED;
   }
-  const size_t need = fa_bwd_workspace_size(B, H, N, d, grad_dtype);
+  const size_t need = fa_bwd_gqa_workspace_size(B, H, Hkv, N, d, grad_dtype);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
   const size_t n = (size_t)B * H * N;
+  const size_t nkv = (size_t)B * Hkv * N;
   const size_t tb = n * d * elem_bytes(dtype);
+  const size_t kvb = nkv * d * elem_bytes(dtype);
   const size_t gb = n * d * elem_bytes(grad_dtype);
-  const Range ins[6] = {range_of(q, tb), range_of(k, tb), range_of(v, tb),
+  const size_t gkvb = nkv * d * elem_bytes(grad_dtype);
+  const Range ins[6] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb),
                         range_of(o, tb), range_of(lse, n * 4), range_of(dO, tb)};
-  const Range outs[4] = {range_of(dq, gb), range_of(dk, gb), range_of(dv, gb), range_of(workspace, need)};
+  const Range outs[4] = {range_of(dq, gb), range_of(dk, gkvb), range_of(dv, gkvb), range_of(workspace, need)};
   for (int i = 0; i < 4; ++i) {
     for (const Range& r : ins)
       if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
@@ -188,8 +210,16 @@ int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* m
   p.dk = dk;
   p.dv = dv;
   p.stats = static_cast<float*>(workspace);
+  p.part_k = nullptr;
+  p.part_v = nullptr;
+  if (Hkv < H) {
+    float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((n * 8 + 255) & ~(size_t)255));
+    p.part_k = part;
+    p.part_v = part + n * d;
+  }
   p.B = B;
   p.H = H;
+  p.Hkv = Hkv;
   p.N = N;
   p.d = d;
   p.scale = scale;
@@ -208,15 +238,22 @@ extern "C" {
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
            void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype, int grad_dtype,
            void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(q, k, v, nullptr, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, dtype, grad_dtype, workspace,
-                  workspace_bytes, stream, false);
+  return bwd_impl(q, k, v, nullptr, o, lse, dO, dq, dk, dv, B, H, H, N, d, scale, causal, dtype, grad_dtype,
+                  workspace, workspace_bytes, stream, false);
+}
+
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+               void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype,
+               int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, nullptr, o, lse, dO, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype, grad_dtype,
+                  workspace, workspace_bytes, stream, false);
 }
 
 int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const unsigned char* block_mask, const void* o,
                        const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                        float scale, int causal, int dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  return bwd_impl(q, k, v, block_mask, o, lse, dO, dq, dk, dv, B, H, N, d, scale, causal, dtype, grad_dtype,
+  return bwd_impl(q, k, v, block_mask, o, lse, dO, dq, dk, dv, B, H, H, N, d, scale, causal, dtype, grad_dtype,
                   workspace, workspace_bytes, stream, true);
 }
 

@@ -124,6 +124,7 @@ struct BwdBf16Args {
   void* dv;
   int grad_bf16;
   int BH;
+  int group;    // query heads per K/V head (1: plain multi-head)
   int N;
   float c;      // |scale| * log2(e), clamped away from 0
   float scale;  // factor of dQ and dK
@@ -199,10 +200,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / a.BH) : (int)(blockIdx.x / a.BH);  // longest rows first
   const int bh = (int)(blockIdx.x % a.BH);
   const size_t hoff = (size_t)bh * (size_t)N * D;
+  const size_t kvoff = (size_t)(bh / a.group) * (size_t)N * D;  // grouped-query: shared K/V head
   const unsigned int head_bytes = (unsigned int)N * D * 2;
   const BufRes qres = make_buf(a.q + hoff, head_bytes);
-  const BufRes kres = make_buf(a.k + hoff, head_bytes);
-  const BufRes vres = make_buf(a.v + hoff, head_bytes);
+  const BufRes kres = make_buf(a.k + kvoff, head_bytes);
+  const BufRes vres = make_buf(a.v + kvoff, head_bytes);
   const BufRes dores = make_buf(a.dO + hoff, head_bytes);
 
   const int q_first = qt * BM;
@@ -548,8 +550,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
     // ---- score wave: K and V rows of this lane's key as MFMA B fragments
     bf16x8 kf[D / 16], vf[D / 16];
     {
-      const BufRes kres = make_buf(a.k + hoff, head_bytes);
-      const BufRes vres = make_buf(a.v + hoff, head_bytes);
+      const size_t kvoff = (size_t)(bh / a.group) * (size_t)N * D;  // grouped-query: shared K/V head
+      const BufRes kres = make_buf(a.k + kvoff, head_bytes);
+      const BufRes vres = make_buf(a.v + kvoff, head_bytes);
       const unsigned int sign = a.neg ? 0x80008000u : 0u;
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
@@ -701,6 +704,7 @@ struct BwdF32Args {
   float* dk;
   float* dv;
   int BH;
+  int group;  // query heads per K/V head
   int N;
   float scale;
 };
@@ -719,12 +723,13 @@ __global__ __launch_bounds__(64) void bwd_f32_dkdv_kernel(BwdF32Args a) {
   const int kt = (int)(blockIdx.x / a.BH);
   const int bh = (int)(blockIdx.x % a.BH);
   const size_t hoff = (size_t)bh * N * D;
+  const size_t kvoff = (size_t)(bh / a.group) * N * D;
   const int k0 = kt * BK;
   for (int idx = tid; idx < BK * D; idx += 64) {
     const int row = idx / D, col = idx % D;
     const int key = k0 + row;
-    kk[row * (D + 1) + col] = key < N ? a.k[hoff + (size_t)key * D + col] : 0.f;
-    vv[row * (D + 1) + col] = key < N ? a.v[hoff + (size_t)key * D + col] : 0.f;
+    kk[row * (D + 1) + col] = key < N ? a.k[kvoff + (size_t)key * D + col] : 0.f;
+    vv[row * (D + 1) + col] = key < N ? a.v[kvoff + (size_t)key * D + col] : 0.f;
   }
   const int key = k0 + tid;
   float gk[D], gv[D];
@@ -784,6 +789,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdF32Args a) {
   const int qt = (int)(blockIdx.x / a.BH);
   const int bh = (int)(blockIdx.x % a.BH);
   const size_t hoff = (size_t)bh * N * D;
+  const size_t kvoff = (size_t)(bh / a.group) * N * D;
   const int qi = qt * BQ + tid;
   const bool in = qi < N;
   float qv[D], dov[D], g[D];
@@ -800,8 +806,8 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdF32Args a) {
     __syncthreads();
     for (int idx = tid; idx < BK * D; idx += 64) {
       const int row = k0 + idx / D;
-      kk[idx] = row < N ? a.k[hoff + (size_t)row * D + idx % D] : 0.f;
-      vv[idx] = row < N ? a.v[hoff + (size_t)row * D + idx % D] : 0.f;
+      kk[idx] = row < N ? a.k[kvoff + (size_t)row * D + idx % D] : 0.f;
+      vv[idx] = row < N ? a.v[kvoff + (size_t)row * D + idx % D] : 0.f;
     }
     __syncthreads();
     if (in && l != -INFINITY) {
@@ -828,8 +834,56 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdF32Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// Grouped-query dK/dV: the per-query-head fp32 gradients [B, H, N, d] are summed
+// over each run of `group` consecutive heads into [B, H_kv, N, d], in head order
+// (deterministic), and written as fp32 or bf16.  HBM-bound: one thread per four
+// output elements, float4 loads of the group's partials.
+// ---------------------------------------------------------------------------
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restrict__ pk, const float* __restrict__ pv,
+                                                            void* __restrict__ dk, void* __restrict__ dv,
+                                                            long long quads, long long head_quads, int group) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * quads) return;
+  const bool is_v = i >= quads;
+  const long long e = is_v ? i - quads : i;  // quad index in [B, H_kv, N, d / 4]
+  const long long kvh = e / head_quads;
+  const long long src = (kvh * group) * head_quads + (e - kvh * head_quads);
+  const float4* p = reinterpret_cast<const float4*>(is_v ? pv : pk) + src;
+  float4 acc = p[0];
+  for (int j = 1; j < group; ++j) {
+    const float4 t = p[(long long)j * head_quads];
+    acc.x += t.x;
+    acc.y += t.y;
+    acc.z += t.z;
+    acc.w += t.w;
+  }
+  void* out = is_v ? dv : dk;
+  if (BF16_OUT) {
+    uint2 pk2;
+    pk2.x = (unsigned int)float_to_bf16_bits(acc.x) | ((unsigned int)float_to_bf16_bits(acc.y) << 16);
+    pk2.y = (unsigned int)float_to_bf16_bits(acc.z) | ((unsigned int)float_to_bf16_bits(acc.w) << 16);
+    reinterpret_cast<uint2*>(out)[e] = pk2;
+  } else {
+    reinterpret_cast<float4*>(out)[e] = acc;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+static void launch_group_sum(const BwdParams& p, hipStream_t stream) {
+  const long long head_quads = (long long)p.N * p.d / 4;
+  const long long quads = (long long)p.B * p.Hkv * head_quads;
+  const unsigned blocks = (unsigned)((2 * quads + 255) / 256);
+  if (p.grad_dtype == 1)
+    hipLaunchKernelGGL((bwd_group_sum_kernel<true>), dim3(blocks), dim3(256), 0, stream, p.part_k, p.part_v, p.dk,
+                       p.dv, quads, head_quads, p.H / p.Hkv);
+  else
+    hipLaunchKernelGGL((bwd_group_sum_kernel<false>), dim3(blocks), dim3(256), 0, stream, p.part_k, p.part_v, p.dk,
+                       p.dv, quads, head_quads, p.H / p.Hkv);
+}
+
 template <typename T, int D>
 static void launch_prep(const BwdParams& p, hipStream_t stream) {
   constexpr int EPT = 16 / sizeof(T);
@@ -853,6 +907,7 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   a.dv = p.dv;
   a.grad_bf16 = p.grad_dtype == 1;
   a.BH = p.B * p.H;
+  a.group = p.H / p.Hkv;
   a.N = p.N;
   a.c = fmaxf(fabsf(p.scale) * kLog2e, 0x1p-100f);
   a.scale = p.scale;
@@ -870,7 +925,14 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_q);
   }
   const unsigned nkb = (unsigned)a.nb;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(nkb * (unsigned)a.BH), dim3(512), dyn_kv, stream, a);
+  BwdBf16Args akv = a;
+  if (a.group > 1) {  // per-query-head fp32 dK / dV, summed over the groups afterwards
+    akv.dk = p.part_k;
+    akv.dv = p.part_v;
+    akv.grad_bf16 = 0;
+  }
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(nkb * (unsigned)a.BH), dim3(512), dyn_kv, stream,
+                     akv);
   const unsigned nqb = (unsigned)((p.N + 255) / 256);
   hipLaunchKernelGGL((bwd_dq_kernel<D, DQ_BN, CAUSAL, SPARSE>), dim3(nqb * (unsigned)a.BH), dim3(512), dyn_q, stream,
                      a);
@@ -886,9 +948,11 @@ static void launch_bwd_f32(const BwdParams& p, hipStream_t stream) {
   a.lse = p.lse;
   a.stats = reinterpret_cast<const float2*>(p.stats);
   a.dq = static_cast<float*>(p.dq);
-  a.dk = static_cast<float*>(p.dk);
-  a.dv = static_cast<float*>(p.dv);
+  const bool grouped = p.Hkv < p.H;
+  a.dk = grouped ? p.part_k : static_cast<float*>(p.dk);
+  a.dv = grouped ? p.part_v : static_cast<float*>(p.dv);
   a.BH = p.B * p.H;
+  a.group = p.H / p.Hkv;
   a.N = p.N;
   a.scale = p.scale;
   const unsigned nk = (unsigned)((p.N + 63) / 64 * a.BH);
@@ -906,6 +970,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
       launch_prep<float, 128>(p, stream);
       if (p.causal) launch_bwd_f32<128, true>(p, stream); else launch_bwd_f32<128, false>(p, stream);
     }
+    if (p.Hkv < p.H) launch_group_sum(p, stream);
     return hipGetLastError();
   }
   const bool sparse = p.mask != nullptr;
@@ -925,6 +990,7 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
       else launch_bwd_bf16<128, false, false>(p, stream);
     }
   }
+  if (p.Hkv < p.H) launch_group_sum(p, stream);
   return hipGetLastError();
 }
 

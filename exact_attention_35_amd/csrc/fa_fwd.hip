@@ -39,6 +39,7 @@ struct FwdKernelArgs {
   float* lse;
   const unsigned char* mask;
   int BH;
+  int group;        // query heads per K/V head (1: plain multi-head)
   int N;
   int nb;           // mask row length (ceil(N / 128))
   float c;          // |scale| * log2(e), clamped away from 0
@@ -176,10 +177,11 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
     bh = (int)(blockIdx.x % a.BH);
   }
   const size_t hoff = (size_t)bh * (size_t)N * D;
+  const size_t kvoff = (size_t)(bh / a.group) * (size_t)N * D;  // grouped-query: shared K/V head
   const unsigned int head_bytes = (unsigned int)N * D * 2;
   const BufRes qres = make_buf(a.q + hoff, head_bytes);
-  const BufRes kres = make_buf(a.k + hoff, head_bytes);
-  const BufRes vres = make_buf(a.v + hoff, head_bytes);
+  const BufRes kres = make_buf(a.k + kvoff, head_bytes);
+  const BufRes vres = make_buf(a.v + kvoff, head_bytes);
   const BufRes ores = make_buf(a.o + hoff, head_bytes);
 
   const int q_first = qt * BM;
@@ -400,6 +402,7 @@ struct FwdF32Args {
   float* o;
   float* lse;
   int BH;
+  int group;
   int N;
   float scale;
 };
@@ -417,6 +420,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdF32Args a) {
   const int bh = (int)(blockIdx.x % a.BH);
   (void)nqt;
   const size_t hoff = (size_t)bh * N * D;
+  const size_t kvoff = (size_t)(bh / a.group) * N * D;
   const int qrow = qt * BM + tid;
   const bool in = qrow < N;
   float qv[D];
@@ -437,8 +441,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdF32Args a) {
       const int key = k0 + row;
       float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
       if (key < N) {
-        kk = *reinterpret_cast<const float4*>(a.k + hoff + (size_t)key * D + col);
-        vv = *reinterpret_cast<const float4*>(a.v + hoff + (size_t)key * D + col);
+        kk = *reinterpret_cast<const float4*>(a.k + kvoff + (size_t)key * D + col);
+        vv = *reinterpret_cast<const float4*>(a.v + kvoff + (size_t)key * D + col);
       }
       *reinterpret_cast<float4*>(ks + row * D + col) = kk;
       *reinterpret_cast<float4*>(vs + row * D + col) = vv;
@@ -489,6 +493,7 @@ static hipError_t launch_fwd_bf16_t(const FwdParams& p, hipStream_t stream) {
   a.lse = p.lse;
   a.mask = p.mask;
   a.BH = p.B * p.H;
+  a.group = p.H / p.Hkv;
   a.N = p.N;
   a.nb = (p.N + 127) / 128;
   const float sa = fabsf(p.scale);
@@ -517,6 +522,7 @@ static hipError_t launch_fwd_f32_t(const FwdParams& p, hipStream_t stream) {
   a.o = static_cast<float*>(p.o);
   a.lse = p.lse;
   a.BH = p.B * p.H;
+  a.group = p.H / p.Hkv;
   a.N = p.N;
   a.scale = p.scale;
   const int nqt = (p.N + 63) / 64;

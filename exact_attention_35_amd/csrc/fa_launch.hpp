@@ -15,6 +15,7 @@ struct FwdParams {
   float* lse;                 // may be null
   const unsigned char* mask;  // block-sparse tile mask, null when dense
   int B, H, N, d;
+  int Hkv;  // K/V heads (divides H); query head h reads K/V head h / (H / Hkv)
   float scale;
   int causal;
   int dtype;  // FA_F32 / FA_BF16
@@ -31,8 +32,13 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* stats;  // workspace: per row of [B, H, N], the pair (lse * log2 e, D = rowsum(dO * O))
+  // workspace, grouped-query only (Hkv < H): fp32 dK and dV of every query head, [B, H, N, d] each,
+  // summed over each group into dk / dv by a final kernel
+  float* part_k;
+  float* part_v;
   const unsigned char* mask;  // block-sparse tile mask (bf16 only), null when dense
   int B, H, N, d;
+  int Hkv;
   float scale;
   int causal;
   int dtype;

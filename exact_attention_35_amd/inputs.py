@@ -9,7 +9,9 @@ The workload shapes stand in for the sequence lengths and head shapes that
 the FlashAttention abstract (Tri Dao's author page on scite.ai) reports
 results for: BERT-large at sequence length 512, GPT-2 at 1K, Path-X at 16K
 and Path-256 at 64K.  Their datasets and weights are not used; iid Gaussian
-activations of the same shapes replace them.
+activations of the same shapes replace them.  The grouped-query workload (the
+FlashAttention-2 variants of the everydayai.blog article) uses the head counts
+of a common 8B decoder, 32 query heads sharing 8 K/V heads, at 16K tokens.
 """
 
 from __future__ import annotations
@@ -41,10 +43,19 @@ class Workload:
     density: float = 0.0  # fraction of strictly-lower off-diagonal tiles kept
     sample_rows: Optional[int] = None  # rows per head the checker evaluates
     backward: bool = False
+    Hkv: Optional[int] = None  # K/V heads (grouped-query); None: as many as query heads
 
     @property
     def shape(self) -> Tuple[int, int, int, int]:
         return (self.B, self.H, self.N, self.d)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hkv is None else self.Hkv
+
+    @property
+    def kv_shape(self) -> Tuple[int, int, int, int]:
+        return (self.B, self.kv_heads, self.N, self.d)
 
     @property
     def scale(self) -> float:
@@ -61,6 +72,7 @@ WORKLOADS = {
         Workload("long_s16k_d128", 4, 1, 16, 16384, 128, "bf16", True, qk_mult=1.7, sample_rows=512),
         Workload("blocksparse_s64k", 5, 2, 16, 65536, 64, "bf16", True, sparse=True,
                  density=1.0 / 16.0, sample_rows=256),
+        Workload("gqa_s16k_h32_kv8_d128", 6, 1, 32, 16384, 128, "bf16", True, sample_rows=256, Hkv=8),
     )
 }
 
@@ -97,11 +109,16 @@ def draw(index: int, slot: int, shape: Sequence[int], mult: float = 1.0, dtype: 
 
 
 def make_qkv(w: Workload, shape: Optional[Sequence[int]] = None):
-    """Q, K, V (and dO when the workload has a backward) as float32 arrays."""
+    """Q, K, V (and dO when the workload has a backward) as float32 arrays.
+
+    `shape` overrides the query shape [B, H, N, d]; K and V then keep the
+    workload's query-to-K/V head ratio (at least one K/V head).
+    """
     shape = tuple(shape) if shape is not None else w.shape
+    kv = (shape[0], max(1, shape[1] * w.kv_heads // w.H), shape[2], shape[3])
     q = draw(w.index, SLOT_Q, shape, w.qk_mult, w.dtype)
-    k = draw(w.index, SLOT_K, shape, w.qk_mult, w.dtype)
-    v = draw(w.index, SLOT_V, shape, 1.0, w.dtype)
+    k = draw(w.index, SLOT_K, kv, w.qk_mult, w.dtype)
+    v = draw(w.index, SLOT_V, kv, 1.0, w.dtype)
     do = draw(w.index, SLOT_DO, shape, 1.0, w.dtype) if w.backward else None
     return q, k, v, do
 
@@ -138,15 +155,18 @@ def sample_rows(N: int, count: int, seed_index: int, head: int = 0) -> np.ndarra
 
 
 def random_case(seed: int, B: int, H: int, N: int, d: int, dtype: str = "bf16", mult: float = 1.0,
-                backward: bool = False):
+                backward: bool = False, h_kv: Optional[int] = None):
     """Small seeded case for edge tests (shapes outside the named workloads).
 
     Q and K are N(0,1) * mult, V (and dO) N(0,1), all rounded to bf16 unless dtype is f32.
+    With h_kv, K and V are [B, h_kv, N, d] (grouped-query).
     """
-    rng = np.random.default_rng(np.random.SeedSequence([SEED_ROOT, 100, seed, B, H, N, d]))
+    key = [SEED_ROOT, 100, seed, B, H, N, d] + ([] if h_kv is None else [h_kv])
+    rng = np.random.default_rng(np.random.SeedSequence(key))
     out = []
     for t in range(4 if backward else 3):
-        x = rng.standard_normal((B, H, N, d), dtype=np.float32)
+        heads = h_kv if (h_kv is not None and t in (1, 2)) else H
+        x = rng.standard_normal((B, heads, N, d), dtype=np.float32)
         if mult != 1.0 and t < 2:  # the multiplier scales Q and K only, as in the named workloads
             x = (x * np.float32(mult)).astype(np.float32)
         out.append(bf16_round(x) if dtype == "bf16" else x)

@@ -46,14 +46,14 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 #define FA_MASK_BLOCK 128 /* rows and keys covered by one block-sparse mask entry */
 
 enum fa_status {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null required pointer, B/H/N < 1, non-finite scale, bad
                               enum, misaligned pointer, output overlapping an input,
-                              or a size whose grid would not fit */
+                              H_kv not a divisor of H, or a size whose grid would not fit */
   FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}; N * d * 4 > 2^31 - 1 (one head's slice is
                               addressed with 32-bit byte offsets); fp32 with block-sparse;
                               a block-sparse N whose tile list does not fit in LDS
@@ -72,6 +72,18 @@ enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 };
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * Grouped-query / multi-query forward (everydayai.blog flash-attention article,
+ * "FlashAttention-2", point 3, lists both variants).  q, o: [B, H, N, d] and lse
+ * [B, H, N] as for fa_fwd; k, v: [B, H_kv, N, d] with H_kv dividing H.  Query
+ * head h attends with key/value head h / (H / H_kv): each run of H / H_kv
+ * consecutive query heads shares one K/V head (H_kv = 1: multi-query; H_kv = H:
+ * identical to fa_fwd).  Same dtypes, limits and errors as fa_fwd, plus
+ * FA_ERR_INVALID_ARG for an H_kv outside [1, H] or not dividing H.
+ */
+int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype, void* stream);
 
 /*
  * Block-sparse forward (FlashAttention abstract: extension to block-sparse
@@ -104,6 +116,28 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int grad_dtype);
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
            void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
            int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of workspace fa_bwd_gqa needs: as fa_bwd_workspace_size(B, H, N, d) when
+ * H_kv == H; otherwise that figure rounded up to 256 bytes plus 8 * B*H*N*d (fp32
+ * dK and dV of every query head before the group sums).  0 for arguments
+ * fa_bwd_gqa would reject.
+ */
+size_t fa_bwd_gqa_workspace_size(int B, int H, int H_kv, int N, int d, int grad_dtype);
+
+/*
+ * Grouped-query / multi-query backward: gradients of L = sum(dO * O) for the
+ * attention of fa_fwd_gqa (same H_kv, scale and causal; o and lse from that
+ * call).  dq: [B, H, N, d]; dk, dv: [B, H_kv, N, d], each the sum over the
+ * group's query heads of that head's gradient (the chain rule through the
+ * shared K/V head).  The per-head fp32 dK/dV are written to the workspace and
+ * summed in head order by a final kernel, so results stay deterministic.
+ * Arguments, dtypes and errors as fa_bwd, the workspace sized by
+ * fa_bwd_gqa_workspace_size().
+ */
+int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+               void* dq, void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal,
+               int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Block-sparse backward.  Gradients of L = sum(dO * O) for the block-sparse

@@ -40,7 +40,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fa_version() == 1
+    assert lib.fa_version() == _lib.FA_ABI_VERSION
+    m = re.search(r"#define FA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == _lib.FA_ABI_VERSION
     for code in (0, -1, -2, -3, -4):
         s = _lib.status_string(code)
         assert s.startswith("FA_") and s != "unknown status"
@@ -136,3 +138,32 @@ def test_workspace_size(lib):
     assert lib.fa_bwd_workspace_size(2, 3, 100, 64, 1) == n * 8
     assert lib.fa_bwd_workspace_size(2, 3, 100, 32, 0) == 0
     assert lib.fa_bwd_workspace_size(0, 3, 100, 64, 0) == 0
+
+
+def test_gqa_validation(lib):
+    q, k, v, o, lse = P, P + MB, P + 2 * MB, P + 3 * MB, P + 4 * MB
+    f = lib.fa_fwd_gqa
+    assert f(q, k, v, o, lse, 1, 8, 3, 64, 64, 0.125, 1, 1, None) == INV  # 3 does not divide 8
+    assert f(q, k, v, o, lse, 1, 8, 0, 64, 64, 0.125, 1, 1, None) == INV
+    assert f(q, k, v, o, lse, 1, 8, 16, 64, 64, 0.125, 1, 1, None) == INV  # more K/V heads than query heads
+    assert f(q, k, v, o, lse, 1, 8, 2, 64, 48, 0.125, 1, 1, None) == UNS
+    # K/V hold H_kv heads: an output just past k's [1, 2, 64, 64] bf16 extent is legal, inside it is not
+    kv_bytes = 2 * 64 * 64 * 2
+    assert f(q, k, v, k + kv_bytes - 16, lse, 1, 8, 2, 64, 64, 0.125, 1, 1, None) == INV
+    ws = lib.fa_bwd_gqa_workspace_size(1, 8, 2, 64, 64, 0)
+    g = lib.fa_bwd_gqa
+    ptrs = [P + i * MB for i in range(9)]
+    assert g(*ptrs, 1, 8, 3, 64, 64, 0.125, 1, 1, 0, P + 10 * MB, ws, None) == INV
+    assert g(*ptrs, 1, 8, 2, 64, 64, 0.125, 1, 1, 0, P + 10 * MB, ws - 16, None) == WS
+    assert g(*ptrs, 1, 8, 2, 64, 64, 0.125, 1, 0, 1, P + 10 * MB, ws, None) == UNS  # bf16 grads of fp32
+    assert g(*ptrs[:7], ptrs[6] + 64, ptrs[8], 1, 8, 2, 64, 64, 0.125, 1, 1, 0, P + 10 * MB, ws, None) == INV
+
+
+def test_gqa_workspace_size(lib):
+    n = 2 * 8 * 100
+    assert lib.fa_bwd_gqa_workspace_size(2, 8, 8, 100, 64, 0) == n * 8 == lib.fa_bwd_workspace_size(2, 8, 100, 64, 0)
+    stats = -(-n * 8 // 256) * 256
+    assert lib.fa_bwd_gqa_workspace_size(2, 8, 2, 100, 64, 1) == stats + 2 * n * 64 * 4
+    assert lib.fa_bwd_gqa_workspace_size(2, 8, 1, 100, 128, 0) == stats + 2 * n * 128 * 4
+    assert lib.fa_bwd_gqa_workspace_size(2, 8, 3, 100, 64, 0) == 0
+    assert lib.fa_bwd_gqa_workspace_size(2, 8, 2, 100, 32, 0) == 0

@@ -1,0 +1,159 @@
+"""GPU parity of grouped-/multi-query attention (fa_fwd_gqa, fa_bwd_gqa) against the fp64 oracle.
+
+K and V carry H_kv heads; query head h reads K/V head h // (H / H_kv).  dK and dV
+of a shared head are sums over its H / H_kv query heads: their rounding errors
+are those of H / H_kv independent per-head gradients, which add like a random
+walk, so the bf16 gate for dK and dV is the per-head gate times sqrt(H / H_kv).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_35_amd import api, inputs
+from gpu_util import TOL_BF16, TOL_F32, TOL_LSE, announce, dev, host, max_err, report
+
+pytestmark = pytest.mark.gpu
+
+BF = torch.bfloat16
+
+
+def run(q, k, v, do, dtype, scale, causal, grad_dtype=torch.float32):
+    tq, tk, tv = dev(q, dtype), dev(k, dtype), dev(v, dtype)
+    o, lse = api.forward(tq, tk, tv, scale, causal)
+    grads = (None, None, None)
+    if do is not None:
+        grads = api.backward(tq, tk, tv, o, lse, dev(do, dtype), scale, causal, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return (host(o), host(lse)) + tuple(None if g is None else host(g) for g in grads)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_bf16(d, causal):
+    for H, hkv in ((8, 2), (4, 1), (6, 3)):
+        for n in (1, 77, 300, 1000):
+            name = f"gqa fwd bf16 H={H} H_kv={hkv} N={n} d={d} causal={causal}"
+            announce(name)
+            q, k, v, _ = inputs.random_case(21, 2, H, n, d, "bf16", mult=1.5, h_kv=hkv)
+            scale = api.default_scale(d)
+            o, lse = run(q, k, v, None, BF, scale, causal)[:2]
+            ro, rl = oracle.forward(q, k, v, scale, causal)
+            e = dict(o=max_err(o, ro), lse=max_err(lse, rl))
+            report(name, **e)
+            assert e["o"] <= TOL_BF16 and e["lse"] <= TOL_LSE, (name, e)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_bf16(d, causal):
+    for H, hkv in ((8, 2), (4, 1)):
+        g = H // hkv
+        for n in (1, 129, 600):
+            name = f"gqa bwd bf16 H={H} H_kv={hkv} N={n} d={d} causal={causal}"
+            announce(name)
+            q, k, v, do = inputs.random_case(22, 1, H, n, d, "bf16", backward=True, h_kv=hkv)
+            scale = api.default_scale(d)
+            _, _, dq, dk, dv = run(q, k, v, do, BF, scale, causal)
+            rdq, rdk, rdv = oracle.backward(q, k, v, do, scale, causal)
+            e = dict(dq=max_err(dq, rdq), dk=max_err(dk, rdk), dv=max_err(dv, rdv))
+            report(name, **e)
+            assert dk.shape == (1, hkv, n, d) and dv.shape == (1, hkv, n, d)
+            assert e["dq"] <= TOL_BF16, (name, e)
+            assert e["dk"] <= TOL_BF16 * math.sqrt(g) and e["dv"] <= TOL_BF16 * math.sqrt(g), (name, e)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_f32(d):
+    for H, hkv in ((4, 2), (3, 1)):
+        for causal in (False, True):
+            name = f"gqa f32 H={H} H_kv={hkv} N=150 d={d} causal={causal}"
+            announce(name)
+            q, k, v, do = inputs.random_case(23, 1, H, 150, d, "f32", backward=True, h_kv=hkv)
+            scale = api.default_scale(d)
+            o, lse, dq, dk, dv = run(q, k, v, do, torch.float32, scale, causal)
+            ro, rl = oracle.forward(q, k, v, scale, causal)
+            rdq, rdk, rdv = oracle.backward(q, k, v, do, scale, causal)
+            e = dict(o=max_err(o, ro), lse=max_err(lse, rl), dq=max_err(dq, rdq), dk=max_err(dk, rdk),
+                     dv=max_err(dv, rdv))
+            report(name, **e)
+            assert max(e.values()) <= TOL_F32, (name, e)
+
+
+def test_bf16_gradient_outputs():
+    """bf16 dK/dV round the fp32 group sum once more: gate at twice the fp32-output bound."""
+    announce("gqa bwd bf16 grads")
+    q, k, v, do = inputs.random_case(24, 2, 8, 512, 128, "bf16", backward=True, h_kv=2)
+    scale = api.default_scale(128)
+    _, _, dq, dk, dv = run(q, k, v, do, BF, scale, True, grad_dtype=BF)
+    rdq, rdk, rdv = oracle.backward(q, k, v, do, scale, True)
+    e = dict(dq=max_err(dq, rdq), dk=max_err(dk, rdk), dv=max_err(dv, rdv))
+    report("gqa bwd bf16 grads", **e)
+    assert e["dq"] <= 2 * TOL_BF16
+    assert max(e["dk"], e["dv"]) <= 2 * TOL_BF16 * math.sqrt(4)
+
+
+def _repeat_equivalence(B, H, hkv, N, d, causal, seed):
+    """fa_*_gqa == fa_* on K/V repeated per query head: bitwise for O, lse and dQ; dK/dV equal
+    the head-order fp32 sums of the dense per-head gradients, bitwise."""
+    g = H // hkv
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(seed)
+    q, do = (torch.randn((B, H, N, d), generator=gen, device="cuda:0").to(BF) for _ in range(2))
+    k, v = (torch.randn((B, hkv, N, d), generator=gen, device="cuda:0").to(BF) for _ in range(2))
+    rk = k.repeat_interleave(g, dim=1).contiguous()
+    rv = v.repeat_interleave(g, dim=1).contiguous()
+    o, lse = api.forward(q, k, v, None, causal)
+    ro, rl = api.forward(q, rk, rv, None, causal)
+    assert torch.equal(o, ro) and torch.equal(lse, rl)
+    dq, dk, dv = api.backward(q, k, v, o, lse, do, None, causal)
+    rdq, rdk, rdv = api.backward(q, rk, rv, ro, rl, do, None, causal)
+    assert torch.equal(dq, rdq)
+    for got, dense in ((dk, rdk), (dv, rdv)):
+        parts = dense.view(B, hkv, g, N, d)
+        acc = parts[:, :, 0].clone()
+        for j in range(1, g):
+            acc += parts[:, :, j]
+        assert torch.equal(got, acc)
+    # bf16 gradients: the same sums, rounded once
+    _, bdk, bdv = api.backward(q, k, v, o, lse, do, None, causal, grad_dtype=BF)
+    assert torch.equal(bdk, dk.to(BF)) and torch.equal(bdv, dv.to(BF))
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_equals_repeated_kv(d):
+    for causal in (False, True):
+        for H, hkv, N in ((8, 2, 1000), (4, 1, 333), (4, 4, 256)):
+            announce(f"gqa == repeated K/V H={H} H_kv={hkv} N={N} d={d} causal={causal}")
+            _repeat_equivalence(2, H, hkv, N, d, causal, 31 + N + d)
+
+
+def test_gqa_workload_full_size():
+    """The 16K, 32-query / 8-K/V-head workload in the launch configuration the benchmark times:
+    O and lse at sampled rows against the oracle, and the whole forward and backward against
+    the dense path on K/V repeated per query head."""
+    w = inputs.WORKLOADS["gqa_s16k_h32_kv8_d128"]
+    announce(w.name)
+    q, k, v, _ = inputs.make_qkv(w)
+    tq, tk, tv = dev(q, BF), dev(k, BF), dev(v, BF)
+    o, lse = api.forward(tq, tk, tv, w.scale, w.causal)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(w.N, w.sample_rows, w.index)
+    heads = [0, 3, 4, 31]
+    g = w.H // w.kv_heads  # oracle rows of the chosen query heads, each with its own K/V head
+    errs = {}
+    for h in heads:
+        ro, rl = oracle.forward_rows(q[:, h:h + 1], k[:, h // g:h // g + 1], v[:, h // g:h // g + 1], rows,
+                                     w.scale, w.causal)
+        errs[f"o_h{h}"] = max_err(host(o[:, h:h + 1, rows]), ro)
+        errs[f"lse_h{h}"] = max_err(host(lse[:, h:h + 1, rows]), rl)
+    report(w.name, **errs)
+    assert all(v_ <= TOL_BF16 for k_, v_ in errs.items() if k_.startswith("o"))
+    assert all(v_ <= TOL_LSE for k_, v_ in errs.items() if k_.startswith("lse"))
+    del tq, tk, tv, o, lse
+    torch.cuda.empty_cache()
+    _repeat_equivalence(w.B, w.H, w.kv_heads, w.N, w.d, w.causal, 35)

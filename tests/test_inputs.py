@@ -66,6 +66,13 @@ def test_sample_rows():
 
 def test_workload_table():
     names = list(inputs.WORKLOADS)
-    assert names == ["tiny_f32", "bert_large_s512", "gpt2_small_s1k", "long_s16k_d128", "blocksparse_s64k"]
+    assert names == ["tiny_f32", "bert_large_s512", "gpt2_small_s1k", "long_s16k_d128", "blocksparse_s64k",
+                     "gqa_s16k_h32_kv8_d128"]
+    g = inputs.WORKLOADS["gqa_s16k_h32_kv8_d128"]
+    assert g.kv_shape == (1, 8, 16384, 128) and g.shape == (1, 32, 16384, 128)
+    q, k, v, _ = inputs.make_qkv(g, (1, 4, 256, 128))
+    assert q.shape == (1, 4, 256, 128) and k.shape == v.shape == (1, 1, 256, 128)
+    q, k, v, do = inputs.random_case(3, 2, 6, 50, 64, backward=True, h_kv=2)
+    assert q.shape == do.shape == (2, 6, 50, 64) and k.shape == v.shape == (2, 2, 50, 64)
     assert inputs.WORKLOADS["tiny_f32"].dtype == "f32"
     assert inputs.WORKLOADS["long_s16k_d128"].scale == np.float32(1.0) / np.sqrt(np.float32(128))
