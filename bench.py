@@ -209,13 +209,13 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel
-    "fwd": {"fetch_kib": 235472.8, "write_kib": 66561.3,
+    "fwd": {"fetch_kib": 241802.4, "write_kib": 66560.0,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "95567a759ef279e6697cbaa67296ec9786ba8fb38e2364661bd0cbfaeb8d1ba3"},
+            "sha256": "f37aed66932d8ff01c312500a5cf448747aa0e2d2929f9b60a760cba65c4920b"},
     # bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel
-    "bwd": {"fetch_kib": 66575.7 + 363891.0 + 337730.7, "write_kib": 2048.0 + 262144.0 + 131072.0,
+    "bwd": {"fetch_kib": 66572.8 + 364047.4 + 327314.6, "write_kib": 2048.0 + 262144.0 + 131072.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "db2de81cad2f33a27bb188f6404f664947a5e7a75042a402cdf4b09a9ecf3f88"},
+            "sha256": "7794b61379fa554c9f75c597b275e64b1a34177bf11f926ba9ec76e07768b3bf"},
 }
 
 
