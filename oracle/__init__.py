@@ -22,6 +22,9 @@ Parity status of each function (how it is pinned, in tests/test_oracle_*.py):
   backward                    -- central finite differences, torch fp64 autograd, invariants
   grouped-/multi-query heads  -- torch fp64 SDPA and autograd with enable_gqa, brute force and
                                  finite differences, K/V heads repeated == plain multi-head
+  fp8 (oracle/fp8.py)         -- e4m3 rounding vs torch float8_e4m3fn; the Hadamard transform vs
+                                 scipy (exact on integers); quantisation vs torch's conversion and
+                                 exponent minimality; the P-rounding bound vs a simulation
 """
 
 from .attention import (  # noqa: F401
@@ -35,3 +38,4 @@ from .attention import (  # noqa: F401
     probabilities,
 )
 from .brute import brute_backward_fd, brute_forward  # noqa: F401
+from . import fp8  # noqa: F401

@@ -143,3 +143,78 @@ def test_planted_mistake_is_caught(name, monkeypatch):
         monkeypatch.setattr(oracle, attr, fn)
     bad = pins.failing_checks(checks)
     assert bad, f"mutation {name} passed every pin"
+
+
+# --------------------------------------------------------------------------- FP8 part
+import oracle_pins_fp8 as pins8  # noqa: E402
+from oracle import fp8 as of8  # noqa: E402
+
+_orig_fwht = of8.fwht_fp32
+_orig_scale_exponent = of8.scale_exponent
+_orig_bound = of8.pv_rounding_bound
+
+
+def _e4m3_round_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a >= 2.0 ** -6, a, 1.0)))
+    step = np.where(a >= 2.0 ** -6, np.exp2(e - 3), 2.0 ** -9)
+    return np.copysign(np.floor(a / step + 0.5) * step, x)  # halves away from zero
+
+
+def _scale_exponent_one_high(amax):
+    return _orig_scale_exponent(amax) + (1 if amax else 0)
+
+
+def _fwht_difference_flipped(x, signs):
+    y = np.array(x, dtype=np.float32) * np.asarray(signs, dtype=np.float32)
+    d = y.shape[-1]
+    h = 1
+    while h < d:
+        v = y.reshape(y.shape[:-1] + (d // (2 * h), 2, h))
+        a = v[..., 0, :].copy()
+        b = v[..., 1, :].copy()
+        v[..., 0, :] = a + b
+        v[..., 1, :] = b - a  # wrong sign
+        h *= 2
+    return y
+
+
+def _fwht_signs_ignored(x, signs):
+    return _orig_fwht(x, np.ones(np.shape(x)[-1]))
+
+
+def _bound_not_normalised(q, k, v, scale, causal=False, rows=None):
+    """The bound without the division by the row sum l."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    N = q.shape[2]
+    rows = np.arange(N) if rows is None else np.asarray(rows)
+    b = _orig_bound(q, k, v, scale, causal, rows)
+    s = scale * np.einsum("bhnd,bhmd->bhnm", q[:, :, rows], np.repeat(k, q.shape[1] // k.shape[1], axis=1))
+    if causal:
+        s = np.where(np.arange(N)[None, :] <= rows[:, None], s, -np.inf)
+    l = np.exp(s - s.max(axis=-1, keepdims=True)).sum(axis=-1)
+    return b * l[..., None]
+
+
+FP8_MUTATIONS = {
+    "e4m3_ties_away_from_zero": ("e4m3_round", _e4m3_round_ties_away),
+    "scale_exponent_one_high": ("scale_exponent", _scale_exponent_one_high),
+    "fwht_difference_flipped": ("fwht_fp32", _fwht_difference_flipped),
+    "rotation_signs_ignored": ("fwht_fp32", _fwht_signs_ignored),
+    "bound_not_normalised": ("pv_rounding_bound", _bound_not_normalised),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_MUTATIONS))
+def test_planted_fp8_mistake_is_caught(name, monkeypatch):
+    attr, fn = FP8_MUTATIONS[name]
+    monkeypatch.setattr(of8, attr, fn)
+    bad = []
+    for c in pins8.FP8_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                c()
+        except (AssertionError, FloatingPointError, ValueError, IndexError):
+            bad.append(c.__name__)
+    assert bad, f"mutation {name} passed every FP8 pin"
