@@ -25,6 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 dense bf16 flop/clk x 2.4 GHz
+PEAK_FP8_TFLOPS = 5033.2   # twice the bf16 rate (dense e4m3 MFMA)
 PEAK_HBM_GBS = 8000.0
 METRIC = "attention fwd/bwd TFLOP/s and % of bf16 MFMA peak, N=512-64K, d=64/128"
 
@@ -42,9 +43,10 @@ def parse():
                          "(H = 16, B = max(1, 32768 / N)), printed as one JSON line")
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="print a text summary of the rocprofv3 CSV output under DIR and exit")
-    ap.add_argument("--only", choices=["step", "fwd", "bwd", "copy"], default="step",
+    ap.add_argument("--only", choices=["step", "fwd", "bwd", "copy", "fp8"], default="step",
                     help="time only one direction (for profiling runs); 'copy' times a plain 512 MiB "
-                         "device-to-device copy, the calibration kernel for the HBM byte counters")
+                         "device-to-device copy, the calibration kernel for the HBM byte counters; 'fp8' "
+                         "times the FP8 path (quantisation of Q, K, V and the FP8 forward) and prints its table")
     return ap.parse_args()
 
 
@@ -132,6 +134,33 @@ def kernel_table():
         del tq, tk, tv
         torch.cuda.empty_cache()
     return rows
+
+
+def fp8_table(steps=10, warmup=2):
+    """The FP8 path on long_s16k_d128: quantisation with incoherent processing (Q, K rotated, V
+    not), HBM-bound, and the FP8 forward, MFMA-bound (peak: dense e4m3)."""
+    import torch
+
+    from exact_attention_35_amd import api, inputs
+
+    w = inputs.WORKLOADS["long_s16k_d128"]
+    q, k, v, _ = inputs.make_qkv(w)
+    tq, tk, tv = to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16)
+    del q, k, v
+    signs = torch.from_numpy(inputs.random_signs(w.d, w.index)).to("cuda:0")
+    q8, k8, v8 = api.quantize_fp8(tq, signs), api.quantize_fp8(tk, signs), api.quantize_fp8(tv)
+    qt_ms = time_calls(lambda: api.quantize_fp8(tq, signs), steps, warmup)
+    qv_ms = time_calls(lambda: api.quantize_fp8(tv), steps, warmup)
+    f_ms = time_calls(lambda: api.forward_fp8(*q8, *k8, *v8, w.scale, w.causal), steps, warmup)
+    n = w.B * w.H * w.N * w.d
+    qbytes = n * 2 + n + w.B * w.H * (-(-w.N // 128)) * 4  # bf16 in, e4m3 codes and scales out
+    ff = flops_fwd(w)
+    return {"workload": w.name, "shape": list(w.shape), "causal": w.causal,
+            "quantize_rotated_ms": round(qt_ms, 4), "quantize_rotated_GBs": round(qbytes / qt_ms / 1e6, 1),
+            "quantize_plain_ms": round(qv_ms, 4), "quantize_plain_GBs": round(qbytes / qv_ms / 1e6, 1),
+            "fwd_fp8_ms": round(f_ms, 4), "fwd_fp8_tflops": round(ff / f_ms / 1e9, 1),
+            "fwd_fp8_frac_fp8_peak": round(ff / f_ms / 1e9 / PEAK_FP8_TFLOPS, 4),
+            "hbm_peak_GBs": PEAK_HBM_GBS, "fp8_peak_tflops": PEAK_FP8_TFLOPS}
 
 
 def sweep():
@@ -294,6 +323,9 @@ def main():
     if args.only == "copy":
         copy_calibration(args)
         return
+    if args.only == "fp8":
+        print(json.dumps({"fp8": fp8_table(args.steps, args.warmup)}), flush=True)
+        return
     w = inputs.WORKLOADS[args.workload]
     assert w.dtype == "bf16" and not w.sparse, "the step times a dense bf16 workload"
     q, k, v, _ = inputs.make_qkv(w)
@@ -382,6 +414,7 @@ def main():
         del tq, tk, tv, tdo, o, lse, ws
         torch.cuda.empty_cache()
         out["workloads"] = kernel_table()
+        out["fp8"] = fp8_table()
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w)
     print(json.dumps(out), flush=True)
 

@@ -19,10 +19,12 @@ FA_ERR_HIP = -4
 FA_F32 = 0
 FA_BF16 = 1
 FA_MASK_BLOCK = 128
-FA_ABI_VERSION = 2  # must equal FA_ABI_VERSION of include/fa.h
+FA_FP8_BLOCK = 128
+FA_ABI_VERSION = 3  # must equal FA_ABI_VERSION of include/fa.h
 
 EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_blocksparse", "fa_bwd_workspace_size", "fa_bwd",
-           "fa_bwd_gqa_workspace_size", "fa_bwd_gqa", "fa_bwd_blocksparse", "fa_status_string", "fa_version")
+           "fa_bwd_gqa_workspace_size", "fa_bwd_gqa", "fa_bwd_blocksparse", "fa_quantize_fp8", "fa_fwd_fp8",
+           "fa_status_string", "fa_version")
 
 _lib = None
 
@@ -71,6 +73,10 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_gqa_workspace_size.argtypes = [_i, _i, _i, _i, _i, _i]
     lib.fa_bwd_gqa.restype = _i
     lib.fa_bwd_gqa.argtypes = [_vp] * 9 + [_i, _i, _i, _i, _i, _f, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
+    lib.fa_quantize_fp8.restype = _i
+    lib.fa_quantize_fp8.argtypes = [_vp] * 4 + [_i] * 5 + [_vp]
+    lib.fa_fwd_fp8.restype = _i
+    lib.fa_fwd_fp8.argtypes = [_vp] * 8 + [_i] * 5 + [_f, _i, _vp]
     lib.fa_bwd_blocksparse.restype = _i
     lib.fa_bwd_blocksparse.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _f, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
     _lib = lib

@@ -182,3 +182,62 @@ class FlashAttentionFunction(torch.autograd.Function):
 def attention(q, k, v, scale=None, causal=False):
     """Differentiable exact attention (bf16 gradients for bf16 inputs); k, v may have H_kv | H heads."""
     return FlashAttentionFunction.apply(q, k, v, scale, causal)
+
+
+def fp8_scale_shape(B: int, H: int, N: int) -> Tuple[int, int, int]:
+    """Shape of the per-block fp8 scales: [B, H, ceil(N / 128)]."""
+    return (B, H, -(-N // _lib.FA_FP8_BLOCK))
+
+
+def quantize_fp8(x: torch.Tensor, signs: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """(codes uint8 [B, H, N, d], scales float32 [B, H, ceil(N/128)]) of x (bf16 or fp32, [B, H, N, d]).
+
+    signs: optional int8 [d] of +-1 on x's device; the rows are then rotated by the
+    randomised Hadamard transform first (incoherent processing; use the same signs
+    for Q and K and none for V).
+    """
+    if x.dim() != 4 or x.dtype not in _DTYPES or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [B, H, N, d] bf16 or float32 GPU tensor")
+    B, H, N, d = x.shape
+    if signs is not None:
+        if signs.dtype != torch.int8 or tuple(signs.shape) != (d,) or signs.device != x.device:
+            raise ValueError(f"signs must be int8 [{d}] on x's device")
+        signs = signs.contiguous()
+    codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(fp8_scale_shape(B, H, N), dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        st = _lib.load().fa_quantize_fp8(x.data_ptr(), None if signs is None else signs.data_ptr(),
+                                         codes.data_ptr(), scales.data_ptr(), B, H, N, d, _DTYPES[x.dtype],
+                                         _stream_ptr(x.device))
+    _lib.check(st, "fa_quantize_fp8")
+    return codes, scales
+
+
+def forward_fp8(q8: torch.Tensor, q_scale: torch.Tensor, k8: torch.Tensor, k_scale: torch.Tensor,
+                v8: torch.Tensor, v_scale: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
+                with_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """FP8 forward on quantize_fp8 outputs: (o bf16 [B, H, N, d], lse fp32 [B, H, N] or None).
+
+    k8, v8 may have H_kv | H heads (grouped-query).
+    """
+    for t in (q8, k8, v8):
+        if t.dim() != 4 or t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.device != q8.device:
+            raise ValueError("q8, k8, v8 must be contiguous uint8 [B, H, N, d] tensors on one GPU")
+    B, H, N, d = q8.shape
+    hkv = k8.shape[1]
+    if v8.shape != k8.shape or k8.shape != (B, hkv, N, d) or hkv < 1 or H % hkv:
+        raise ValueError(f"q8, k8, v8 shapes do not fit: {tuple(q8.shape)} {tuple(k8.shape)} {tuple(v8.shape)}")
+    for name, t, heads in (("q_scale", q_scale, H), ("k_scale", k_scale, hkv), ("v_scale", v_scale, hkv)):
+        if (tuple(t.shape) != fp8_scale_shape(B, heads, N) or t.dtype != torch.float32 or not t.is_contiguous()
+                or t.device != q8.device):
+            raise ValueError(f"{name} must be contiguous float32 {fp8_scale_shape(B, heads, N)} on q8's device")
+    scale = default_scale(d) if scale is None else float(scale)
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if with_lse else None
+    with torch.cuda.device(q8.device):
+        st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
+                                    k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(),
+                                    None if lse is None else lse.data_ptr(), B, H, hkv, N, d, scale,
+                                    int(bool(causal)), _stream_ptr(q8.device))
+    _lib.check(st, "fa_fwd_fp8")
+    return o, lse

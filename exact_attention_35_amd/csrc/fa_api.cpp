@@ -258,3 +258,86 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const unsign
 }
 
 }  // extern "C"
+
+namespace {
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_quantize_fp8(const void* x, const signed char* signs, unsigned char* codes, float* scales, int B, int H,
+                    int N, int d, int dtype, void* stream) {
+  int st = check_common(B, H, N, d, 1.0f, 0, dtype);
+  if (st != FA_OK) return st;
+  if (!x || !codes || !scales) return FA_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(codes) || !aligned4(scales)) return FA_ERR_INVALID_ARG;
+  const size_t n = (size_t)B * H * N;
+  const size_t nb = ((size_t)N + FA_FP8_BLOCK - 1) / FA_FP8_BLOCK;
+  if ((size_t)B * H * nb > (size_t)kMaxGrid) return FA_ERR_INVALID_ARG;
+  const Range rx = range_of(x, n * d * elem_bytes(dtype));
+  const Range rc = range_of(codes, n * d);
+  const Range rs = range_of(scales, (size_t)B * H * nb * 4);
+  if (overlap(rx, rc) || overlap(rx, rs) || overlap(rc, rs)) return FA_ERR_INVALID_ARG;
+  if (signs) {
+    const Range rg = range_of(signs, (size_t)d);
+    if (overlap(rg, rc) || overlap(rg, rs)) return FA_ERR_INVALID_ARG;
+  }
+  fa::Fp8QuantParams p;
+  p.x = x;
+  p.dtype = dtype;
+  p.signs = signs;
+  p.codes = codes;
+  p.scales = scales;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  const hipError_t e = fa::launch_fp8_quantize(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsigned char* v, const float* q_scale,
+               const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H, int H_kv, int N, int d,
+               float scale, int causal, void* stream) {
+  int st = check_common(B, H, N, d, scale, causal, FA_BF16);
+  if (st != FA_OK) return st;
+  if (!valid_kv_heads(H, H_kv)) return FA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !q_scale || !k_scale || !v_scale || !o) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return FA_ERR_INVALID_ARG;
+  if (!aligned4(q_scale) || !aligned4(k_scale) || !aligned4(v_scale)) return FA_ERR_INVALID_ARG;
+  const size_t n = (size_t)B * H * N;
+  const size_t nkv = (size_t)B * H_kv * N;
+  const size_t nb = ((size_t)N + FA_FP8_BLOCK - 1) / FA_FP8_BLOCK;
+  const Range ins[6] = {range_of(q, n * d), range_of(k, nkv * d), range_of(v, nkv * d),
+                        range_of(q_scale, (size_t)B * H * nb * 4), range_of(k_scale, (size_t)B * H_kv * nb * 4),
+                        range_of(v_scale, (size_t)B * H_kv * nb * 4)};
+  const Range ro = range_of(o, n * d * 2);
+  for (const Range& r : ins) {
+    if (overlap(ro, r)) return FA_ERR_INVALID_ARG;
+    if (lse && overlap(range_of(lse, n * 4), r)) return FA_ERR_INVALID_ARG;
+  }
+  if (lse && overlap(range_of(lse, n * 4), ro)) return FA_ERR_INVALID_ARG;
+  fa::Fp8FwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.qs = q_scale;
+  p.ks = k_scale;
+  p.vs = v_scale;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.Hkv = H_kv;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.causal = causal;
+  const hipError_t e = fa::launch_fp8_fwd(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

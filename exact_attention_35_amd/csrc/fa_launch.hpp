@@ -45,7 +45,33 @@ struct BwdParams {
   int grad_dtype;
 };
 
+// FP8 path (e4m3 codes, per-128-row block scales)
+struct Fp8QuantParams {
+  const void* x;
+  int dtype;                 // FA_F32 / FA_BF16
+  const signed char* signs;  // null: no rotation
+  unsigned char* codes;
+  float* scales;
+  int B, H, N, d;
+};
+
+struct Fp8FwdParams {
+  const unsigned char* q;
+  const unsigned char* k;
+  const unsigned char* v;
+  const float* qs;
+  const float* ks;
+  const float* vs;
+  void* o;     // bf16
+  float* lse;  // may be null
+  int B, H, Hkv, N, d;
+  float scale;
+  int causal;
+};
+
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream);
+hipError_t launch_fp8_quantize(const Fp8QuantParams& p, hipStream_t stream);
+hipError_t launch_fp8_fwd(const Fp8FwdParams& p, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 
 }  // namespace fa

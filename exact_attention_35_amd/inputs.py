@@ -183,3 +183,12 @@ def random_block_mask(seed: int, nb: int, density: float, causal: bool) -> np.nd
     if causal:
         mask = np.tril(mask)
     return mask
+
+
+SLOT_SIGNS = 6  # random signs of the fp8 rotation
+
+
+def random_signs(d: int, seed_index: int) -> np.ndarray:
+    """int8 [d] of +-1: the random signs of the randomised Hadamard rotation (incoherent processing)."""
+    rng = rng_for(seed_index, SLOT_SIGNS)
+    return np.where(rng.random(d) < 0.5, -1, 1).astype(np.int8)

@@ -46,8 +46,9 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 #define FA_MASK_BLOCK 128 /* rows and keys covered by one block-sparse mask entry */
+#define FA_FP8_BLOCK 128  /* rows of one head that share one fp8 scale */
 
 enum fa_status {
   FA_OK = 0,
@@ -153,6 +154,46 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const unsign
                        const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
                        int B, int H, int N, int d, float scale, int causal, int dtype, int grad_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * FP8 quantisation with incoherent processing (everydayai.blog flash-attention
+ * article, "FlashAttention-3": FP8 support, and incoherent processing to reduce
+ * quantisation error).  x: [B, H, N, d] in dtype (FA_BF16 or FA_F32), finite.
+ * codes: uint8 [B, H, N, d], OCP E4M3 (bias 7, largest finite 448, no
+ * infinities); scales: fp32 [B, H, ceil(N/128)], one per block of FA_FP8_BLOCK
+ * consecutive rows of a head.  Per block, with y the block's rows: the exponent
+ * e is the smallest integer with max|y| * 2^-e <= 448 (0 for an all-zero block),
+ * codes = round-to-nearest-even of y * 2^-e, scale = 2^e (times fl32(1/sqrt(d))
+ * when rotating), so that code * scale approximates the row.
+ * signs: NULL, or a device array of d int8 values (negative = -1, else +1): the
+ * rows are then rotated first, y = x diag(signs) H_d with the Sylvester Hadamard
+ * matrix H_d, by the fast Walsh-Hadamard transform in fp32 (stages of pair
+ * distance 1, 2, 4, ..., d/2 in that order; this fixes every rounding).  Rotate
+ * Q and K with the same signs and V not at all: (Q M)(K M)^T = Q K^T for the
+ * orthogonal M = diag(signs) H_d / sqrt(d), so fa_fwd_fp8 then computes the
+ * attention of the unrotated inputs.  Pointers 16-byte aligned (scales 4-byte);
+ * outputs must not overlap inputs.
+ */
+int fa_quantize_fp8(const void* x, const signed char* signs, unsigned char* codes, float* scales,
+                    int B, int H, int N, int d, int dtype, void* stream);
+
+/*
+ * FP8 forward: o (bf16 [B, H, N, d]) and lse (fp32 [B, H, N], may be NULL) of
+ * exact attention of the dequantised inputs code * scale, computed with the
+ * e4m3 matrix cores.  q, q_scale as written by fa_quantize_fp8 for [B, H, N, d];
+ * k, v, k_scale, v_scale for [B, H_kv, N, d] (H_kv divides H; grouped-query as in
+ * fa_fwd_gqa).  Scales must be positive and finite.  Two roundings go beyond
+ * the dequantised inputs.  (1) The matrix cores sum each group of 64 fp8
+ * products of S = Q K^T with an error of up to about 2^-11 of the group's
+ * largest product (then accumulate in fp32).  (2) P = exp(S - running row
+ * maximum) is rounded to e4m3 for the P V product (the row sums use the
+ * unrounded P): |dO| <= (2^-4 sum_{P >= 2^-6} P |v| + 2^-10 sum_{P < 2^-6} |v|)
+ * / sum P per element.  O is rounded to bf16.
+ * Arguments and errors as fa_fwd_gqa.
+ */
+int fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsigned char* v,
+               const float* q_scale, const float* k_scale, const float* v_scale, void* o, float* lse,
+               int B, int H, int H_kv, int N, int d, float scale, int causal, void* stream);
 
 /* Static, human-readable name of a status code ("unknown status" otherwise). */
 const char* fa_status_string(int status);

@@ -29,7 +29,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -167,3 +167,27 @@ def test_gqa_workspace_size(lib):
     assert lib.fa_bwd_gqa_workspace_size(2, 8, 1, 100, 128, 0) == stats + 2 * n * 128 * 4
     assert lib.fa_bwd_gqa_workspace_size(2, 8, 3, 100, 64, 0) == 0
     assert lib.fa_bwd_gqa_workspace_size(2, 8, 2, 100, 32, 0) == 0
+
+
+def test_fp8_validation(lib):
+    x, c, s, g = P, P + MB, P + 2 * MB, P + 3 * MB
+    f = lib.fa_quantize_fp8
+    assert f(None, g, c, s, 1, 2, 300, 64, 1, None) == INV
+    assert f(x, g, None, s, 1, 2, 300, 64, 1, None) == INV
+    assert f(x, g, c, None, 1, 2, 300, 64, 1, None) == INV
+    assert f(x, g, c, s, 1, 2, 300, 96, 1, None) == UNS
+    assert f(x, g, c, s, 1, 2, 300, 64, 7, None) == INV
+    assert f(x, g, c + 8, s, 1, 2, 300, 64, 1, None) == INV      # misaligned codes
+    assert f(x, g, c, s + 2, 1, 2, 300, 64, 1, None) == INV      # misaligned scales
+    assert f(x, g, x + 64, s, 1, 2, 300, 64, 1, None) == INV     # codes overlap x
+    assert f(x, g, c, c + 16, 1, 2, 300, 64, 1, None) == INV     # scales inside codes
+    h = lib.fa_fwd_fp8
+    q, k, v, qs, ks, vs, o, lse = (P + i * MB for i in range(8))
+    assert h(q, k, v, qs, ks, vs, o, lse, 1, 4, 3, 256, 64, 0.1, 1, None) == INV  # 3 does not divide 4
+    assert h(q, k, v, qs, ks, vs, o, lse, 1, 4, 2, 256, 80, 0.1, 1, None) == UNS
+    assert h(q, k, v, None, ks, vs, o, lse, 1, 4, 2, 256, 64, 0.1, 1, None) == INV
+    assert h(q, k, v, qs, ks, vs, None, lse, 1, 4, 2, 256, 64, 0.1, 1, None) == INV
+    assert h(q, k, v, qs, ks, vs, o, lse, 1, 4, 2, 256, 64, math.nan, 1, None) == INV
+    assert h(q, k, v, qs, ks, vs, q + 32, lse, 1, 4, 2, 256, 64, 0.1, 1, None) == INV  # o overlaps q
+    assert h(q, k, v, qs, ks, vs, o, o + 16, 1, 4, 2, 256, 64, 0.1, 1, None) == INV    # lse inside o
+    assert h(q, k, v, qs + 1, ks, vs, o, lse, 1, 4, 2, 256, 64, 0.1, 1, None) == INV  # misaligned scale
