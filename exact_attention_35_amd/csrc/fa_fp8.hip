@@ -73,30 +73,57 @@ struct QuantArgs {
   float rnorm;  // fl32(1 / sqrt(d)) when rotating, else 1
 };
 
-template <int D>
+template <int D, bool F32>
 __global__ __launch_bounds__(128) void quant_fp8_kernel(QuantArgs a) {
+  // The block's rows move between HBM and LDS in coalesced 16-byte pieces (thread t
+  // takes pieces t, t + 128, ...); each lane then works on one row in registers.
+  // Rows are padded by 16 bytes in LDS so that the 64 lanes' row reads spread over
+  // the banks.
+  constexpr int XROW = D * (F32 ? 4 : 2) + 16;  // LDS bytes per input row
+  constexpr int CROW = D + 16;              // LDS bytes per code row
+  __shared__ __align__(16) unsigned char xs[128 * XROW];
   __shared__ float wmax[2];
+  const int tid = (int)threadIdx.x;
   const int blk = (int)blockIdx.x;  // bh * nb + block
   const int bh = blk / a.nb;
-  const int row = (blk - bh * a.nb) * 128 + (int)threadIdx.x;
-  const bool in = row < a.N;
-  const size_t off = ((size_t)bh * a.N + (in ? row : 0)) * D;
+  const int r0 = (blk - bh * a.nb) * 128;
+  const int rows = min(128, a.N - r0);
+  const int row = r0 + tid;
+  const bool in = tid < rows;
+  constexpr int rbytes = D * (F32 ? 4 : 2);
+  {
+    // every load of the thread is issued before the first LDS store, so that all of
+    // them are in flight together
+    constexpr int PT = rbytes / 16;  // 16-byte pieces per thread (= per row)
+    const unsigned char* src = static_cast<const unsigned char*>(a.x) + ((size_t)bh * a.N + r0) * rbytes;
+    const int pieces = rows * PT;
+    uint4 v[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int i = tid + 128 * j;
+      v[j] = i < pieces ? *reinterpret_cast<const uint4*>(src + 16 * (size_t)i) : zero_uint4();
+    }
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int i = tid + 128 * j;
+      *reinterpret_cast<uint4*>(xs + (i / PT) * XROW + 16 * (i % PT)) = v[j];
+    }
+  }
+  __syncthreads();
   float y[D];
-  if (a.x_f32) {
-    const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + off);
+  if (F32) {
 #pragma unroll
     for (int i = 0; i < D / 4; ++i) {
-      const float4 f = in ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 f = in ? *reinterpret_cast<const float4*>(xs + tid * XROW + 16 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
       y[4 * i] = f.x;
       y[4 * i + 1] = f.y;
       y[4 * i + 2] = f.z;
       y[4 * i + 3] = f.w;
     }
   } else {
-    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const unsigned short*>(a.x) + off);
 #pragma unroll
     for (int i = 0; i < D / 8; ++i) {
-      const uint4 u = in ? src[i] : zero_uint4();
+      const uint4 u = in ? *reinterpret_cast<const uint4*>(xs + tid * XROW + 16 * i) : zero_uint4();
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[8 * i + e] = bf16_bits_to_float(bf16_lane_of(u, e));
     }
@@ -122,8 +149,8 @@ __global__ __launch_bounds__(128) void quant_fp8_kernel(QuantArgs a) {
   for (int i = 0; i < D; ++i) m = fmaxf(m, fabsf(y[i]));
 #pragma unroll
   for (int s = 32; s > 0; s >>= 1) m = fmaxf(m, __shfl_xor(m, s));
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();  // also: every lane has read its row, so xs can take the codes
   const float amax = fmaxf(wmax[0], wmax[1]);
   // smallest e with amax 2^-e <= 448 = 0.875 2^9 (exact: frexp splits amax into mantissa and exponent)
   int e = 0;
@@ -132,9 +159,7 @@ __global__ __launch_bounds__(128) void quant_fp8_kernel(QuantArgs a) {
     const float mant = frexpf(amax, &ex);
     e = mant <= 0.875f ? ex - 9 : ex - 8;
   }
-  if (threadIdx.x == 0) a.scales[blk] = ldexpf(a.rnorm, e);
-  if (!in) return;
-  uint4* dst = reinterpret_cast<uint4*>(a.codes + off);
+  if (tid == 0) a.scales[blk] = ldexpf(a.rnorm, e);
 #pragma unroll
   for (int i = 0; i < D / 16; ++i) {
     unsigned int w[4];
@@ -145,8 +170,26 @@ __global__ __launch_bounds__(128) void quant_fp8_kernel(QuantArgs a) {
       v = cvt_fp8x2<true>(ldexpf(p[2], -e), ldexpf(p[3], -e), v);
       w[j] = (unsigned int)v;
     }
-    dst[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    *reinterpret_cast<uint4*>(xs + tid * CROW + 16 * i) = make_uint4(w[0], w[1], w[2], w[3]);
   }
+  __syncthreads();
+  {
+    constexpr int PT = D / 16;
+    unsigned char* dst = a.codes + ((size_t)bh * a.N + r0) * D;
+    const int pieces = rows * PT;
+    uint4 v[PT];
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int i = tid + 128 * j;
+      v[j] = *reinterpret_cast<const uint4*>(xs + (i / PT) * CROW + 16 * (i % PT));
+    }
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+      const int i = tid + 128 * j;
+      if (i < pieces) *reinterpret_cast<uint4*>(dst + 16 * (size_t)i) = v[j];
+    }
+  }
+  (void)row;
 }
 
 // ---------------------------------------------------------------------------
@@ -551,10 +594,13 @@ hipError_t launch_fp8_quantize(const Fp8QuantParams& p, hipStream_t stream) {
   a.nb = (p.N + 127) / 128;
   a.rnorm = p.signs != nullptr ? (float)(1.0 / sqrt((double)p.d)) : 1.0f;
   const dim3 grid((unsigned)((size_t)p.B * p.H * a.nb));
-  if (p.d == 64)
-    hipLaunchKernelGGL((quant_fp8_kernel<64>), grid, dim3(128), 0, stream, a);
-  else
-    hipLaunchKernelGGL((quant_fp8_kernel<128>), grid, dim3(128), 0, stream, a);
+  if (p.d == 64) {
+    if (a.x_f32) hipLaunchKernelGGL((quant_fp8_kernel<64, true>), grid, dim3(128), 0, stream, a);
+    else hipLaunchKernelGGL((quant_fp8_kernel<64, false>), grid, dim3(128), 0, stream, a);
+  } else {
+    if (a.x_f32) hipLaunchKernelGGL((quant_fp8_kernel<128, true>), grid, dim3(128), 0, stream, a);
+    else hipLaunchKernelGGL((quant_fp8_kernel<128, false>), grid, dim3(128), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

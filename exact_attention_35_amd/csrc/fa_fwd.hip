@@ -69,32 +69,40 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[BN / 32], int k_first, int
   }
 }
 
-// row maximum of the tile for this lane's query (both half-waves)
+// row maximum of the tile for this lane's query (both half-waves); four
+// independent v_max3 chains, so that one wave's dependent maxima do not stall it
 template <int BN>
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[BN / 32]) {
-  float m = max3f(s[0][0], s[0][1], s[0][2]);
+  constexpr int NE = 16 * (BN / 32);  // scores per lane: 32 or 64
+  constexpr int Q = NE / 4;           // per chain: 8 or 16 (even)
+  float m[4];
 #pragma unroll
-  for (int i = 3; i + 1 < 16 * (BN / 32); i += 2) m = max3f(m, s[i >> 4][i & 15], s[(i + 1) >> 4][(i + 1) & 15]);
-  m = max2f(m, s[BN / 32 - 1][15]);
-  return xhalf_max(m);
+  for (int c = 0; c < 4; ++c) {
+    const int b = c * Q;
+    m[c] = max2f(s[b >> 4][b & 15], s[(b + 1) >> 4][(b + 1) & 15]);
+#pragma unroll
+    for (int i = 2; i < Q; i += 2)
+      m[c] = max3f(m[c], s[(b + i) >> 4][(b + i) & 15], s[(b + i + 1) >> 4][(b + i + 1) & 15]);
+  }
+  return xhalf_max(max2f(max3f(m[0], m[1], m[2]), m[3]));
 }
 
 // P~ = exp2(S c - m c) -> bf16 MFMA fragments; returns the fp32 row sum of this half-wave
 template <int BN>
 __device__ __forceinline__ float exp_tile(const f32x16 (&s)[BN / 32], float c, float mc, bf16x8 (&pf)[BN / 16]) {
-  float lsum = 0.f;
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: no serial add chain
 #pragma unroll
   for (int t = 0; t < BN / 16; ++t) {
     bf16x8 frag;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float p = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][8 * (t & 1) + e], c, -mc));
-      lsum += p;
+      lsum[e & 3] += p;
       frag[e] = (__bf16)p;
     }
     pf[t] = frag;
   }
-  return lsum;
+  return (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
 }
 
 // Schedule of one MFMA phase: LDS fragment reads run ahead of the MFMAs
