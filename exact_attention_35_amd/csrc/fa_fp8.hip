@@ -25,8 +25,10 @@
 //   * S^T = K Q^T: lane (query, half h) gets 16 keys of each 32-key block; K rows
 //     sit in LDS permuted so that the two blocks of a 64-key group give lane h
 //     exactly keys 32h .. 32h+31 in order, which are the k-slots of the P.V MFMA;
-//   * P = exp2(S c_t - m) relative to the exact running maximum (the largest P
-//     is 1, exactly representable), rounded to e4m3 by v_cvt_pk_fp8_f32;
+//   * P = exp2(S c_t - m) relative to a basis m that trails the running row
+//     maximum by less than one binade (P <= 2, far inside e4m3's range; the
+//     accumulator is rescaled only when the maximum passes m + 1), rounded to
+//     e4m3 by v_cvt_pk_fp8_f32;
 //   * O^T += V^T P^T, V^T read from the natural-order V tile by ds_read_b64_tr_b8
 //     (each lane receives one d column of 8 keys per read);
 //   * the per-block K scale enters the tile's score factor c_t = c qs ks_t; the
@@ -516,7 +518,9 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8FwdArgs a) {
     const float ct = fmaxf(cq * ks[blk], 0x1p-100f);
     const float vt = vs[blk];
     const float mt = tile_max8<BN>(s) * ct;
-    const bool grow = mt > m2;
+    // the basis moves only when the maximum exceeds it by more than one binade, so P <= 2
+    // (far inside e4m3's range) and most tiles skip the accumulator rescale
+    const bool grow = mt > m2 + 1.f;
     float alpha = 1.f;
     if (grow) {
       alpha = __builtin_amdgcn_exp2f(m2 - mt);

@@ -185,9 +185,9 @@ int fa_quantize_fp8(const void* x, const signed char* signs, unsigned char* code
  * fa_fwd_gqa).  Scales must be positive and finite.  Two roundings go beyond
  * the dequantised inputs.  (1) The matrix cores sum each group of 64 fp8
  * products of S = Q K^T with an error of up to about 2^-11 of the group's
- * largest product (then accumulate in fp32).  (2) P = exp(S - running row
- * maximum) is rounded to e4m3 for the P V product (the row sums use the
- * unrounded P): |dO| <= (2^-4 sum_{P >= 2^-6} P |v| + 2^-10 sum_{P < 2^-6} |v|)
+ * largest product (then accumulate in fp32).  (2) P = exp(S - m), with m
+ * within one binade below the running row maximum, is rounded to e4m3 for the
+ * P V product (the row sums use the unrounded P): |dO| <= (2^-4 sum_{P >= 2^-6} P |v| + 2^-10 sum_{P < 2^-6} |v|)
  * / sum P per element.  O is rounded to bf16.
  * Arguments and errors as fa_fwd_gqa.
  */

@@ -24,9 +24,10 @@ readings below are the ones used (each is listed in the design notes):
   1/sqrt(d) goes into the scale.  fp32 and this stage order are the precision
   in which the codes are decided, so both sides reproduce them bit for bit.
 * The FP8 forward is exact attention of the dequantised Q, K, V (`forward_fp8`);
-  the kernel additionally rounds P to e4m3 (relative to the running row maximum,
-  so the largest P is exactly 1) before P.V.  `pv_rounding_bound` bounds what that
-  rounding can change.
+  the kernel additionally rounds P to e4m3 before P.V, with P taken relative to a
+  basis at or below the running row maximum (so P >= its value relative to the
+  final maximum, and P stays far below 448).  `pv_rounding_bound` bounds what that
+  rounding can change for any such basis.
 
 Parity status: e4m3 rounding, encoding and decoding are pinned against torch's
 float8_e4m3fn conversions; the transform against scipy's Hadamard matrix (exactly,
@@ -155,8 +156,9 @@ def forward_fp8(q8, qs, k8, ks, v8, vs, scale, causal=False):
 def pv_rounding_bound(q, k, v, scale, causal=False, rows=None):
     """Per-element bound of |O_kernel - O| caused by rounding P to e4m3, for float64 inputs.
 
-    With P_ij = exp(s_ij - m_i) (m_i the row maximum, so P <= 1, and the running
-    maximum of the kernel only makes its P larger), rounding P to e4m3 moves it
+    With P_ij = exp(s_ij - m_i) (m_i the row maximum, so P <= 1; a kernel basis at
+    or below it only makes its P larger, by the factor its result is later scaled
+    down with), rounding P to e4m3 moves it
     by at most 2^-4 P for P >= 2^-6 and by at most 2^-10 below; O_i divides by
     l_i = sum_j P_ij, which the kernel sums from the unrounded P.  Hence
       |dO_ic| <= (2^-4 sum_{P_ij >= 2^-6} P_ij |v_jc| + 2^-10 sum_{P_ij < 2^-6} |v_jc|) / l_i.
