@@ -70,6 +70,39 @@ def to_dev(x, dtype):
     return torch.from_numpy(x).to(dtype).to("cuda:0")
 
 
+def time_launches(fn, n, warmup=2, flush=None):
+    """Sorted per-launch times (ms): HIP events around each of n back-to-back calls on the
+    stream (one synchronisation at the end, so the GPU never idles between them); `flush`
+    is enqueued, untimed, before each call."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for s, e in ev:
+        if flush is not None:
+            flush()
+        s.record()
+        fn()
+        e.record()
+    torch.cuda.synchronize()
+    return sorted(s.elapsed_time(e) for s, e in ev)
+
+
+def gemm_reference(n=8192, reps=20):
+    """bf16 GEMM n x n x n through torch (hipBLASLt): a clock-honest reference rate for the
+    matrix cores under a sustained load on this machine (context for the fraction of peak)."""
+    import torch
+
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda:0", dtype=torch.bfloat16)
+    ts = time_launches(lambda: torch.matmul(a, b, out=c), reps, warmup=10)
+    med = ts[len(ts) // 2]
+    return {"shape": [n, n, n], "median_ms": round(med, 4), "tflops": round(2.0 * n ** 3 / med / 1e9, 1)}
+
+
 def time_calls(fn, n, warmup=2):
     """Average duration (ms) of fn() measured with HIP events on torch's current stream."""
     import torch
@@ -122,6 +155,17 @@ def kernel_table():
         else:
             ms = time_calls(lambda: api.forward(tq, tk, tv, w.scale, w.causal), 20)
             entry.update(fwd_ms=ms, fwd_tflops=flops_fwd(w) / ms / 1e9)
+            ts = time_launches(lambda: api.forward(tq, tk, tv, w.scale, w.causal), 20)
+            entry.update(fwd_median_ms=ts[len(ts) // 2], fwd_min_ms=ts[0])
+            if w.N <= 1024:
+                # the inputs fit in the 256 MB last-level cache: also time each launch after
+                # writing a 512 MB buffer, so that they come from HBM
+                junk = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+                tc = time_launches(lambda: api.forward(tq, tk, tv, w.scale, w.causal), 10,
+                                   flush=lambda: junk.fill_(1))
+                entry.update(fwd_cold_median_ms=tc[len(tc) // 2],
+                             fwd_cold_tflops=flops_fwd(w) / tc[len(tc) // 2] / 1e9)
+                del junk
             if w.backward or w.name == "long_s16k_d128" or w.Hkv is not None:
                 o, lse = api.forward(tq, tk, tv, w.scale, w.causal)
                 tdo = to_dev(inputs.draw(w.index, inputs.SLOT_DO, w.shape), torch.bfloat16)
@@ -285,7 +329,8 @@ def profile_summary(d):
             agg[(r["Counter_Name"], r["Kernel_Name"])].append(float(r["Counter_Value"]))
         lines.append(f"pmc ({os.path.relpath(f, d)}):")
         for (c, k), v in agg.items():
-            lines.append(f"  {c:>10} {len(v):3d} dispatches, mean {sum(v) / len(v):12.1f} KiB  {k[:90]}")
+            unit = " KiB" if c in ("FETCH_SIZE", "WRITE_SIZE") else ""
+            lines.append(f"  {c:>10} {len(v):3d} dispatches, mean {sum(v) / len(v):16.1f}{unit}  {k[:90]}")
     return "\n".join(lines)
 
 
@@ -415,6 +460,10 @@ def main():
         torch.cuda.empty_cache()
         out["workloads"] = kernel_table()
         out["fp8"] = fp8_table()
+        g = gemm_reference()
+        g["fwd_frac_of_gemm"] = None if fwd_ms is None else round(f_fwd / fwd_ms / 1e9 / g["tflops"], 4)
+        g["bwd_frac_of_gemm"] = None if bwd_ms is None else round(f_bwd / bwd_ms / 1e9 / g["tflops"], 4)
+        out["gemm_reference"] = g
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w)
     print(json.dumps(out), flush=True)
 
