@@ -166,6 +166,21 @@ def kernel_table():
                 entry.update(fwd_cold_median_ms=tc[len(tc) // 2],
                              fwd_cold_tflops=flops_fwd(w) / tc[len(tc) // 2] / 1e9)
                 del junk
+                # launch-bound at this size: 10 forwards captured in one HIP graph and replayed
+                o_g = torch.empty_like(tq)
+                l_g = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    api.forward(tq, tk, tv, w.scale, w.causal, out=o_g, lse_out=l_g)
+                torch.cuda.current_stream().wait_stream(side)
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    for _ in range(10):
+                        api.forward(tq, tk, tv, w.scale, w.causal, out=o_g, lse_out=l_g)
+                gms = time_calls(graph.replay, 10) / 10
+                entry.update(fwd_graph_ms=gms, fwd_graph_tflops=flops_fwd(w) / gms / 1e9)
+                del graph, o_g, l_g
             if w.backward or w.name == "long_s16k_d128" or w.Hkv is not None:
                 o, lse = api.forward(tq, tk, tv, w.scale, w.causal)
                 tdo = to_dev(inputs.draw(w.index, inputs.SLOT_DO, w.shape), torch.bfloat16)

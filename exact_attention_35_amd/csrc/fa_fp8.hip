@@ -241,6 +241,7 @@ struct Fp8Cfg {
   static constexpr int NDC = D / 64;                  // 64-wide d chunks of S^T = K Q^T
   static constexpr int BM = 256;
   static_assert(LPW * 4 * 1024 == TILE, "a tile is a whole number of 1 KB loads per wave");
+  static_assert(128 % BN == 0, "a key tile lies inside one 128-row K/V scale block");
 };
 
 template <int D, int BN>
@@ -632,10 +633,10 @@ static hipError_t launch_fp8_fwd_t(const Fp8FwdParams& p, hipStream_t stream) {
 
 hipError_t launch_fp8_fwd(const Fp8FwdParams& p, hipStream_t stream) {
   (void)hipGetLastError();
-  // 8 KB tiles: 64 keys at d = 128, 128 keys at d = 64
+  // 128-key tiles (one K/V scale block each): 16 KB at d = 128, 8 KB at d = 64
   if (p.d == 64)
     return p.causal ? launch_fp8_fwd_t<64, 128, true>(p, stream) : launch_fp8_fwd_t<64, 128, false>(p, stream);
-  return p.causal ? launch_fp8_fwd_t<128, 64, true>(p, stream) : launch_fp8_fwd_t<128, 64, false>(p, stream);
+  return p.causal ? launch_fp8_fwd_t<128, 128, true>(p, stream) : launch_fp8_fwd_t<128, 128, false>(p, stream);
 }
 
 }  // namespace fa
