@@ -297,11 +297,11 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel
-    "fwd": {"fetch_kib": 241802.4, "write_kib": 66560.0,
+    "fwd": {"fetch_kib": 243715.9, "write_kib": 66560.0,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "f37aed66932d8ff01c312500a5cf448747aa0e2d2929f9b60a760cba65c4920b"},
+            "sha256": "e92a9c0b8f5c2202e922dc100f2638c471a9738e8e4828ce32220cea8a5a901c"},
     # bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel
-    "bwd": {"fetch_kib": 66572.8 + 364047.4 + 327314.6, "write_kib": 2048.0 + 262144.0 + 131072.0,
+    "bwd": {"fetch_kib": 66572.9 + 363596.3 + 307456.3, "write_kib": 2048.0 + 262144.0 + 131072.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
             "sha256": "7794b61379fa554c9f75c597b275e64b1a34177bf11f926ba9ec76e07768b3bf"},
 }
