@@ -299,21 +299,28 @@ MEASURED_TRAFFIC = {
     # fwd_bf16_kernel
     "fwd": {"fetch_kib": 243715.9, "write_kib": 66560.0,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "e92a9c0b8f5c2202e922dc100f2638c471a9738e8e4828ce32220cea8a5a901c"},
+            "sha256": "ccf533d0ba746f472d51da26fc80f1bd1f13445f41181b7847b9d799e7abf7ea"},
     # bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel
     "bwd": {"fetch_kib": 66572.9 + 363596.3 + 307456.3, "write_kib": 2048.0 + 262144.0 + 131072.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "7794b61379fa554c9f75c597b275e64b1a34177bf11f926ba9ec76e07768b3bf"},
+            "sha256": "6ef45d89768e2e666fda623c8183ec4285bb85afb4fdc957b46f6e0c33f5f6b3"},
 }
 
 
 def sources_sha256(names):
+    """sha256 of the sources with comments and blank lines removed (a comment edit
+    does not change the kernels the figures were measured on)."""
     import hashlib
+    import re
 
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "exact_attention_35_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "exact_attention_35_amd", "csrc", n), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [l.rstrip() for l in text.splitlines() if l.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()
 
 

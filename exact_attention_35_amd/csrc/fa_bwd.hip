@@ -19,7 +19,9 @@
 // Each gradient is owned by exactly one workgroup, so there are no atomics
 // and the results are deterministic; the price is that S and dP are
 // recomputed by both the dK/dV and the dQ kernel (seven tile contractions per
-// (query, key) tile pair instead of five).
+// (query, key) tile pair instead of five).  Grouped-query heads: the dK/dV
+// kernel writes each query head's fp32 dK, dV to the workspace and
+// bwd_group_sum_kernel adds each group's heads in head order.
 #include <math.h>
 
 #include <type_traits>

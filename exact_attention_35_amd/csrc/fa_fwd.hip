@@ -7,22 +7,24 @@
 // softmax results; "The Flash Attention Algorithm": block sizes from on-chip
 // memory, results written back to HBM once per block).
 //
-// bf16 kernel, one workgroup = 128 queries of one (b, h), 4 waves x 32 queries:
+// bf16 kernel (fwd_bf16_kernel), one workgroup = 256 queries of one (b, h),
+// 8 waves x 32 queries:
 //   * the wave's Q rows live in VGPRs for the whole kernel (MFMA B operand);
-//   * K/V tiles of BN keys stream HBM -> VGPR -> LDS, double-buffered, one
-//     barrier per tile; V is transposed on the way into LDS so that P.V reads
-//     16-byte key-contiguous fragments;
+//   * K/V tiles of BN keys (16 KB) arrive by LDS-direct buffer loads into rings
+//     of three buffers, two tiles ahead of use;
 //   * S^T = K Q^T on bf16 MFMA puts one query per lane (16 keys per lane, the
 //     other 16 in lane ^ 32), so the row max/sum is in-lane plus one exchange;
+//     K rows sit in LDS permuted so that P converts to the next MFMA's operand
+//     in registers;
 //   * online softmax in the base-2 domain, rescaling the running output only
 //     when the row maximum grows by more than 2^8 (exact: the final division
 //     uses the same basis);
-//   * O^T += V^T P^T on bf16 MFMA, P converted to bf16 straight from the
-//     accumulator registers (K rows are stored permuted so that no shuffle is
-//     needed);
+//   * O^T += V^T P^T on bf16 MFMA, V^T read with transposing LDS reads;
+//   * waves w and w+4 share a SIMD and alternate MFMA and softmax phases;
 //   * epilogue: O = acc / l, lse = m * |scale| + ln l (natural log).
-// Block-sparse: the workgroup first compacts its row of the 128x128 tile mask
-// into a list of key tiles in LDS, then visits only those.
+// Grouped-query heads read K/V head bh / group.  Block-sparse: each half of the
+// workgroup lists the key tiles kept by its 128-row mask row and visits only
+// those.  fwd_f32_kernel is a plain fp32 kernel (one query per thread).
 #include <math.h>
 
 #include "fa_device.hpp"
