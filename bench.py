@@ -223,7 +223,7 @@ def fp8_table(steps=10, warmup=2):
 
 
 def sweep():
-    """TFLOP/s of fa_fwd and fa_bwd over the metric's range of sequence lengths and head dims.
+    """TFLOP/s of fa_fwd, fa_bwd and fa_fwd_fp8 over the metric's range of sequence lengths and head dims.
 
     H = 16 and B = max(1, 32768 / N) heads of iid N(0, 1) bf16 activations drawn on
     the device from a seeded generator (only timed, never checked here).
@@ -247,15 +247,22 @@ def sweep():
                 n_it = max(3, min(20, int(2e12 / (4.0 * B * H * N * N * d))))
                 f_ms = time_calls(lambda: api.forward(q, k, v, None, causal, out=o, lse_out=lse), n_it)
                 b_ms = time_calls(lambda: api.backward(q, k, v, o, lse, do, None, causal, workspace=ws), n_it)
+                # FP8 forward on the same inputs (Q, K rotated), quantisation outside the timing
+                signs = torch.where(torch.rand(d, generator=gen, device="cuda:0") < 0.5, -1, 1).to(torch.int8)
+                q8, k8, v8 = api.quantize_fp8(q, signs), api.quantize_fp8(k, signs), api.quantize_fp8(v)
+                f8_ms = time_calls(lambda: api.forward_fp8(*q8, *k8, *v8, None, causal), n_it)
                 fl = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
                 rows.append({"N": N, "d": d, "causal": causal, "B": B, "H": H,
                              "fwd_ms": round(f_ms, 4), "fwd_tflops": round(fl / f_ms / 1e9, 1),
                              "fwd_frac_peak": round(fl / f_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
                              "bwd_ms": round(b_ms, 4), "bwd_tflops": round(2.5 * fl / b_ms / 1e9, 1),
-                             "bwd_frac_peak": round(2.5 * fl / b_ms / 1e9 / PEAK_BF16_TFLOPS, 4)})
+                             "bwd_frac_peak": round(2.5 * fl / b_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                             "fwd_fp8_ms": round(f8_ms, 4), "fwd_fp8_tflops": round(fl / f8_ms / 1e9, 1),
+                             "fwd_fp8_frac_fp8_peak": round(fl / f8_ms / 1e9 / PEAK_FP8_TFLOPS, 4)})
                 print(f"sweep N={N} d={d} causal={causal}: fwd {rows[-1]['fwd_tflops']} TFLOP/s, "
-                      f"bwd {rows[-1]['bwd_tflops']} TFLOP/s", file=sys.stderr, flush=True)
-                del q, k, v, do, o, lse, ws
+                      f"bwd {rows[-1]['bwd_tflops']} TFLOP/s, fwd fp8 {rows[-1]['fwd_fp8_tflops']} TFLOP/s",
+                      file=sys.stderr, flush=True)
+                del q, k, v, do, o, lse, ws, q8, k8, v8
                 torch.cuda.empty_cache()
     return rows
 
