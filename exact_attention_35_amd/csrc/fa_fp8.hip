@@ -241,7 +241,8 @@ struct Fp8Cfg {
   static constexpr int NDC = D / 64;                  // 64-wide d chunks of S^T = K Q^T
   static constexpr int BM = 256;
   static_assert(LPW * 4 * 1024 == TILE, "a tile is a whole number of 1 KB loads per wave");
-  static_assert(128 % BN == 0, "a key tile lies inside one 128-row K/V scale block");
+  static constexpr int NH = BN > 128 ? BN / 128 : 1;  // 128-row K/V scale blocks per tile
+  static_assert(128 % BN == 0 || BN % 128 == 0, "a key tile covers whole scale blocks or lies inside one");
 };
 
 template <int D, int BN>
@@ -312,14 +313,24 @@ __device__ __forceinline__ void qk_tile8(const unsigned char* kbuf, const int (&
 
 // O^T += V^T P^T: d block db, 64-key group g; the V^T operand (keys 64g + 32h + j for
 // byte j, d = 32 db + lane % 32) comes from four transposing reads of 8 keys each.
+// A 256-key tile spans two V scale blocks: the accumulator, expressed in the first
+// block's scale, is multiplied by `mid` (first / second scale) before the second
+// half is added (a uniform branch, taken only when the two scales differ).
 template <int D, int BN>
 __device__ __forceinline__ void pv_tile8(const unsigned char* vbuf, const int (&vo)[D / 32],
-                                         const i32x8 (&pf)[BN / 64], f32x16 (&oacc)[D / 32]) {
+                                         const i32x8 (&pf)[BN / 64], f32x16 (&oacc)[D / 32], float mid) {
   int o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = fresh(vo[db]);
 #pragma unroll
   for (int g = 0; g < BN / 64; ++g) {
+    if (BN > 128 && g == 2 && mid != 1.f) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= mid;
+      }
+    }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const unsigned char* p = vbuf + 64 * g * D + o[db];
@@ -349,22 +360,33 @@ __device__ __forceinline__ void mask_tile8(f32x16 (&s)[BN / 32], int k_first, in
   }
 }
 
-template <int BN>
-__device__ __forceinline__ float tile_max8(const f32x16 (&s)[BN / 32]) {
-  float m = max3f(s[0][0], s[0][1], s[0][2]);
+// this lane's maximum of S ct over the tile (ct per 128-key scale block), across both half-waves
+template <int BN, int NH>
+__device__ __forceinline__ float tile_max8(const f32x16 (&s)[BN / 32], const float (&ct)[NH]) {
+  constexpr int NB = BN / 32 / NH;  // 32-key blocks per scale block
+  float mt = -INFINITY;
 #pragma unroll
-  for (int i = 3; i + 1 < 16 * (BN / 32); i += 2) m = max3f(m, s[i >> 4][i & 15], s[(i + 1) >> 4][(i + 1) & 15]);
-  m = max2f(m, s[BN / 32 - 1][15]);
-  return xhalf_max(m);
+  for (int h = 0; h < NH; ++h) {
+    const int b0 = h * NB;
+    float m = max3f(s[b0][0], s[b0][1], s[b0][2]);
+#pragma unroll
+    for (int i = 3; i + 1 < 16 * NB; i += 2)
+      m = max3f(m, s[b0 + (i >> 4)][i & 15], s[b0 + ((i + 1) >> 4)][(i + 1) & 15]);
+    m = max2f(m, s[b0 + NB - 1][15]);
+    mt = NH == 1 ? m * ct[0] : max2f(mt, m * ct[h]);
+  }
+  return xhalf_max(mt);
 }
 
 // P = exp2(S ct - mc) -> e4m3 fragments (byte 16b' + r of fragment g from block 2g + b');
 // returns the fp32 sum of this half-wave's P
-template <int BN>
-__device__ __forceinline__ float exp_tile8(const f32x16 (&s)[BN / 32], float ct, float mc, i32x8 (&pf)[BN / 64]) {
+template <int BN, int NH>
+__device__ __forceinline__ float exp_tile8(const f32x16 (&s)[BN / 32], const float (&cts)[NH], float mc,
+                                           i32x8 (&pf)[BN / 64]) {
   float lsum = 0.f;
 #pragma unroll
   for (int g = 0; g < BN / 64; ++g) {
+    const float ct = cts[(2 * g) / (BN / 32 / NH)];  // the scale block of this 64-key group
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       const int b = 2 * g + (w >> 2);
@@ -480,6 +502,8 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8FwdArgs a) {
   float m2 = -INFINITY;  // running row maximum of S c_t (log2 units)
   float l_half = 0.f;
   float vbase = 1.f;  // V scale the accumulator is expressed in
+  float pv_mid = 1.f;   // for the pending P.V of a two-block tile: first / second V scale,
+  float pv_vlast = 1.f; // and the second one
   f32x16 s[NSB];
   i32x8 pf[NPG];
 #pragma unroll
@@ -505,7 +529,8 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8FwdArgs a) {
 
   auto gemm_phase = [&](int t, const unsigned char* kcur, const unsigned char* vprev) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
-    pv_tile8<D, BN>(vprev, vo, pf, oacc);
+    pv_tile8<D, BN>(vprev, vo, pf, oacc, pv_mid);
+    if (C::NH > 1) vbase = pv_vlast;  // the accumulator is now in the second block's scale
     qk_tile8<D, BN>(kcur, ko, qf, s);
     sched_gemm_phase8<D, BN>();
     if (t < ntiles) {
@@ -515,10 +540,22 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8FwdArgs a) {
     __builtin_amdgcn_s_setprio(0);
   };
   auto softmax_phase = [&](int t) __attribute__((always_inline)) {
+    constexpr int NH = C::NH;
     const int blk = (tile_at(t) * BN) >> 7;
-    const float ct = fmaxf(cq * ks[blk], 0x1p-100f);
-    const float vt = vs[blk];
-    const float mt = tile_max8<BN>(s) * ct;
+    float ct[NH];
+    float vh[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int bi = min(blk + h, a.nb - 1);  // a second block wholly past N only holds masked keys
+      ct[h] = fmaxf(cq * ks[bi], 0x1p-100f);
+      vh[h] = vs[bi];
+    }
+    const float vt = vh[0];
+    if (NH > 1) {
+      pv_mid = vh[0] / vh[NH - 1];
+      pv_vlast = vh[NH - 1];
+    }
+    const float mt = tile_max8<BN, NH>(s, ct);
     // the basis moves only when the maximum exceeds it by more than one binade, so P <= 2
     // (far inside e4m3's range) and most tiles skip the accumulator rescale
     const bool grow = mt > m2 + 1.f;
@@ -537,7 +574,7 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8FwdArgs a) {
       vbase = vt;
     }
     const float mc = m2 == -INFINITY ? 0.f : m2;
-    l_half = l_half * alpha + exp_tile8<BN>(s, ct, mc, pf);
+    l_half = l_half * alpha + exp_tile8<BN, NH>(s, ct, mc, pf);
   };
   auto step = [&](int t, const unsigned char* kcur, unsigned char* knext2, const unsigned char* vprev,
                   unsigned char* vnext) __attribute__((always_inline)) {
@@ -633,9 +670,12 @@ static hipError_t launch_fp8_fwd_t(const Fp8FwdParams& p, hipStream_t stream) {
 
 hipError_t launch_fp8_fwd(const Fp8FwdParams& p, hipStream_t stream) {
   (void)hipGetLastError();
-  // 128-key tiles (one K/V scale block each): 16 KB at d = 128, 8 KB at d = 64
-  if (p.d == 64)
+  // 16 KB tiles: 128 keys (one K/V scale block) at d = 128, 256 keys (two) at d = 64 -- except
+  // for short sequences, where the half-empty last tile of 256 keys costs more than it saves
+  if (p.d == 64 && p.N <= 2048)
     return p.causal ? launch_fp8_fwd_t<64, 128, true>(p, stream) : launch_fp8_fwd_t<64, 128, false>(p, stream);
+  if (p.d == 64)
+    return p.causal ? launch_fp8_fwd_t<64, 256, true>(p, stream) : launch_fp8_fwd_t<64, 256, false>(p, stream);
   return p.causal ? launch_fp8_fwd_t<128, 128, true>(p, stream) : launch_fp8_fwd_t<128, 128, false>(p, stream);
 }
 

@@ -115,7 +115,9 @@ def _check_fwd(name, q8, k8, v8, scale, causal, rows=None):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_forward_fp8(d, causal):
-    for n in (1, 77, 300, 1000):
+    # at d = 64, N <= 2048 runs 128-key tiles and longer sequences 256-key tiles (two K/V
+    # scale blocks per tile): 2600 covers the latter with a ragged last tile
+    for n in (1, 77, 300, 1000) + ((2600,) if d == 64 else ()):
         for rotate in (False, True):
             name = f"fp8 fwd N={n} d={d} causal={causal} rotate={rotate}"
             announce(name)
