@@ -304,13 +304,13 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel
-    "fwd": {"fetch_kib": 243715.9, "write_kib": 66560.0,
+    "fwd": {"fetch_kib": 236632.4, "write_kib": 66560.0,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "ccf533d0ba746f472d51da26fc80f1bd1f13445f41181b7847b9d799e7abf7ea"},
+            "sha256": "901deb5cff475037254ecd7774f52b93459e13bbff671096f14778d4f2cde362"},
     # bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel
-    "bwd": {"fetch_kib": 66572.9 + 363596.3 + 307456.3, "write_kib": 2048.0 + 262144.0 + 131072.0,
+    "bwd": {"fetch_kib": 66575.4 + 362755.4 + 316869.5, "write_kib": 2048.0 + 262144.0 + 131072.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "6ef45d89768e2e666fda623c8183ec4285bb85afb4fdc957b46f6e0c33f5f6b3"},
+            "sha256": "9641265b01a61770bf0a8b1d84cfc8a0e4b272611d9f23f3861fccfea306c583"},
 }
 
 

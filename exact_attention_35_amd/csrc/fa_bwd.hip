@@ -571,15 +571,25 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
     const KOffsets<D> ko = k_offsets<D>(l32, half);
     f32x16 s[NSB], dp[NSB];
     bf16x8 pf[NPT], dsf[NPT];
-    auto score_mfma = [&](const unsigned short* qb, const unsigned short* ob) __attribute__((always_inline)) {
+    // S = K Q^T of one tile (from zero) and dP - D = V dO^T - D (from dp = -D, set by p_body)
+    auto s_mfma = [&](const unsigned short* qb) __attribute__((always_inline)) {
       __builtin_amdgcn_s_setprio(1);
-      qk_pair_tile<D, BQ>(qb, ob, ko, kf, vf, s, dp);
-      sched_one_read_per_mfma<2 * NSB * (D / 16)>();
+#pragma unroll
+      for (int b = 0; b < NSB; ++b) s[b] = zero16();
+      qk_ring_tile<D, BQ>(qb, ko, kf, s);
+      sched_one_read_per_mfma<NSB * (D / 16)>();
       __builtin_amdgcn_s_setprio(0);
     };
-    // P and dS of tile i (register r of block b is query 32b + acc_row_swapped(r, half))
-    // the masked variant is a separate copy so that the common path has no per-element selects
-    auto score_body = [&](int q0, const float2* st, auto mask_tag) __attribute__((always_inline)) {
+    auto dp_mfma = [&](const unsigned short* ob) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_setprio(1);
+      qk_ring_tile<D, BQ>(ob, ko, vf, dp);
+      sched_one_read_per_mfma<NSB * (D / 16)>();
+      __builtin_amdgcn_s_setprio(0);
+    };
+    // P of tile i (register r of block b is query 32b + acc_row_swapped(r, half)), kept in s
+    // as fp32 for dS and packed for the handover; dp starts at -D of the same query.
+    // The masked variant is a separate copy so that the common path has no per-element selects.
+    auto p_body = [&](int q0, const float2* st, auto mask_tag) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(mask_tag)::value;
 #pragma unroll
       for (int b = 0; b < NSB; ++b) {
@@ -598,50 +608,59 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * g + e;
             float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -sd[e].x));
-            float ds = p * (dp[b][r] - sd[e].y);
             if (MASKED) {
               // query = base + off with off = 16(r/8) + (r%8) a constant
               const int base = q0 + 32 * b + 8 * half;
               const int off = 16 * (r >> 3) + (r & 7);
               const bool hide = off >= N - base || (CAUSAL && off < mykey - base);
               p = hide ? 0.f : p;
-              ds = hide ? 0.f : ds;
             }
             s[b][r] = p;
-            dp[b][r] = ds;
+            dp[b][r] = -sd[e].y;
           }
         }
       }
 #pragma unroll
-      for (int t2 = 0; t2 < NPT; ++t2) {
-        pf[t2] = pack_bf16(s[t2 >> 1], 8 * (t2 & 1));
-        dsf[t2] = pack_bf16(dp[t2 >> 1], 8 * (t2 & 1));
-      }
+      for (int t2 = 0; t2 < NPT; ++t2) pf[t2] = pack_bf16(s[t2 >> 1], 8 * (t2 & 1));
     };
-    auto score_vector = [&](int i, const float2* st) __attribute__((always_inline)) {
+    auto p_vector = [&](int i, const float2* st) __attribute__((always_inline)) {
       const int q0 = i < T ? tile_q(i) * BQ : N;  // past the last tile: everything masked
-      if ((q0 + BQ > N) || (CAUSAL && q0 < wave_k0 + 31)) score_body(q0, st, std::true_type{});
-      else score_body(q0, st, std::false_type{});
+      if ((q0 + BQ > N) || (CAUSAL && q0 < wave_k0 + 31)) p_body(q0, st, std::true_type{});
+      else p_body(q0, st, std::false_type{});
     };
-    // Step i: phase a hands over dS(i) and runs the MFMAs of tile i+1; phase b
-    // computes P(i+1), dS(i+1) and hands over P(i+1).  Unconditional, so that no
-    // value lives across a handover: at i + 1 = T the tile is past N and every P
-    // and dS of it is masked to zero.
+    // dS = P (dP - D); a masked P is 0, and so is its dS (dP - D is finite)
+    auto ds_vector = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int b = 0; b < NSB; ++b) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[b][r] *= s[b][r];
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < NPT; ++t2) dsf[t2] = pack_bf16(dp[t2 >> 1], 8 * (t2 & 1));
+    };
+    // Step i: phase a computes and hands over dS(i), then runs S(i+1); phase b
+    // computes and hands over P(i+1), then runs dP(i+1).  The two phases carry the
+    // same MFMA count, and each SIMD's gradient wave adds 16 MFMAs to both.
+    // Unconditional, so that no value lives across a handover: at i + 1 = T the tile
+    // is past N and every P (hence dS) of it is masked to zero.
     auto step = [&](int i, const unsigned short* qnxt, const unsigned short* onxt, const float2* snxt)
                     __attribute__((always_inline)) {
+      ds_vector();
 #pragma unroll
       for (int t2 = 0; t2 < NPT; ++t2) xch[sw][NPT + t2][lane] = as_uint4(dsf[t2]);
-      score_mfma(qnxt, onxt);
+      s_mfma(qnxt);
       barrier_ring<15>();  // the dS handover writes have completed
-      score_vector(i + 1, snxt);
+      p_vector(i + 1, snxt);
 #pragma unroll
       for (int t2 = 0; t2 < NPT; ++t2) xch[sw][t2][lane] = as_uint4(pf[t2]);
+      dp_mfma(onxt);
       barrier_ring<15>();  // the P handover writes have completed
     };
-    score_mfma(qbuf_0, obuf_0);
-    score_vector(0, st_0);
+    s_mfma(qbuf_0);
+    p_vector(0, st_0);
 #pragma unroll
     for (int t2 = 0; t2 < NPT; ++t2) xch[sw][t2][lane] = as_uint4(pf[t2]);
+    dp_mfma(obuf_0);
     barrier_ring<15>();
     for (int i = 0; i < T; i += 3) {
       step(i, qbuf_1, obuf_1, st_1);

@@ -157,6 +157,31 @@ __device__ __forceinline__ void qk_pair_tile(const unsigned short* buf1, const u
   }
 }
 
+// One row-read tile product S += X F (tile in the K layout), its LDS operands loaded
+// PF MFMAs ahead into a register ring.  S is not cleared: the caller sets its start.
+template <int D, int BN, int PF = 4>
+__device__ __forceinline__ void qk_ring_tile(const unsigned short* buf, const KOffsets<D>& ko,
+                                             const bf16x8 (&f)[D / 16], f32x16 (&s)[BN / 32]) {
+  constexpr int NSB = BN / 32;
+  constexpr int NM = NSB * (D / 16);
+  // MFMA m: chunk cc = m / NSB, block b = m % NSB
+  int o[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) o[cc] = fresh(ko.off[cc]);
+  auto operand = [&](int m) __attribute__((always_inline)) -> bf16x8 {
+    return lds_bf16x8(buf + 32 * (m % NSB) * D + o[m / NSB]);
+  };
+  bf16x8 ring[PF];
+#pragma unroll
+  for (int m = 0; m < PF; ++m) ring[m] = operand(m);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const bf16x8 x = ring[m % PF];
+    if (m + PF < NM) ring[m % PF] = operand(m + PF);
+    s[m % NSB] = mfma32(x, f[m / NSB], s[m % NSB]);
+  }
+}
+
 // Per-lane element offsets of the transposing V reads: base (row part) and one
 // chunk offset per 32-wide d block.
 template <int D>
