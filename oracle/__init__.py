@@ -22,6 +22,8 @@ Parity status of each function (how it is pinned, in tests/test_oracle_*.py):
   backward                    -- central finite differences, torch fp64 autograd, invariants
   grouped-/multi-query heads  -- torch fp64 SDPA and autograd with enable_gqa, brute force and
                                  finite differences, K/V heads repeated == plain multi-head
+  bf16_backward_bound         -- holds for a step-by-step simulation of a bf16 kernel's roundings,
+                                 and is not vacuous (oracle/bounds.py)
   fp8 (oracle/fp8.py)         -- e4m3 rounding vs torch float8_e4m3fn; the Hadamard transform vs
                                  scipy (exact on integers); quantisation vs torch's conversion and
                                  exponent minimality; the P-rounding bound vs a simulation
@@ -38,4 +40,5 @@ from .attention import (  # noqa: F401
     probabilities,
 )
 from .brute import brute_backward_fd, brute_forward  # noqa: F401
+from .bounds import bf16_backward_bound  # noqa: F401
 from . import fp8  # noqa: F401

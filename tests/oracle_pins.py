@@ -417,7 +417,61 @@ def check_gqa_backward(seed=14):
                 assert np.max(np.abs(a - r.reshape(2, hkv, g, 19, 6).sum(axis=2))) <= 1e-12
 
 
+def _bf16(x):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).to(
+        torch.float64).numpy()
+
+
+def _simulate_bf16_backward(q, k, v, do, scale, causal):
+    """A bf16 kernel's arithmetic, step by step: fp32 evaluation, P rounded to bf16 for P.V
+    and P^T dO, O stored in bf16 and used for D, dS rounded to bf16 for dQ and dK."""
+    f32 = np.float32
+    B, H, N, d = q.shape
+    out = [np.zeros((B, H, N, d)) for _ in range(3)]
+    for b in range(B):
+        for h in range(H):
+            kh = oatt.kv_head(h, H, k.shape[1])
+            Q, K, V, dO = (a.astype(f32) for a in (q[b, h], k[b, kh], v[b, kh], do[b, h]))
+            s = (f32(scale) * (Q @ K.T)).astype(f32)
+            if causal:
+                s = np.where(np.arange(N)[None, :] <= np.arange(N)[:, None], s, f32(-np.inf))
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m).astype(f32)
+            l = p.sum(axis=1, keepdims=True, dtype=f32)
+            O = _bf16((_bf16(p).astype(f32) @ V) / l).astype(f32)        # stored forward output
+            lse = (m + np.log(l)).astype(f32)
+            P = np.exp(s - lse).astype(f32)                               # recomputed from lse
+            D = np.sum(dO * O, axis=1, keepdims=True, dtype=f32)
+            dS = _bf16(P * ((dO @ V.T).astype(f32) - D)).astype(f32)
+            out[0][b, h] = f32(scale) * (dS @ K)
+            out[1][b, h] = f32(scale) * (dS.T @ Q)
+            out[2][b, h] = _bf16(P).astype(f32).T @ dO
+    return out
+
+
+def check_bf16_backward_bound(seed=16):
+    """The bf16 rounding bound holds for a step-by-step simulation of the roundings it is
+    about, on diffuse and peaked rows, causal or not, and is not vacuous."""
+    worst = 0.0
+    for mult, causal in ((1.0, False), (1.7, True), (3.0, True), (0.3, False)):
+        q, k, v, do = (_rand(seed + t, (1, 2, 96, 16), mult if t < 2 else 1.0) for t in range(4))
+        q, k, v, do = (_bf16(a) for a in (q, k, v, do))
+        scale = 0.25
+        ref = oracle.backward(q, k, v, do, scale, causal)
+        sim = _simulate_bf16_backward(q, k, v, do, scale, causal)
+        bnd = oracle.bf16_backward_bound(q, k, v, do, scale, causal)
+        for g, r, e in zip(sim, ref, bnd):
+            err = np.abs(g - r)
+            assert np.all(err <= e), float(np.max(err - e))
+            worst = max(worst, float(np.max(err / e)))
+            assert np.median(err / e) > 1e-3, float(np.median(err / e))
+    assert worst > 0.5, worst  # the bound is reached within a factor of 2
+
+
 BACKWARD_CHECKS = [
+    check_bf16_backward_bound,
     check_finite_differences,
     check_torch_autograd,
     check_backward_invariants,

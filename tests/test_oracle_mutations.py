@@ -218,3 +218,22 @@ def test_planted_fp8_mistake_is_caught(name, monkeypatch):
         except (AssertionError, FloatingPointError, ValueError, IndexError):
             bad.append(c.__name__)
     assert bad, f"mutation {name} passed every FP8 pin"
+
+
+# --------------------------------------------------------------------------- bf16 backward bound
+from oracle import bounds as obnd  # noqa: E402
+
+_orig_u = obnd.U_BF16
+
+
+@pytest.mark.parametrize("name,attr,value", [
+    ("bf16_unit_roundoff_halved", "U_BF16", _orig_u / 2.0),   # the fraction-bit count off by one
+    ("bf16_unit_roundoff_doubled", "U_BF16", _orig_u * 2.0),  # loose enough to be near-vacuous
+])
+def test_planted_bound_mistake_is_caught(name, attr, value, monkeypatch):
+    monkeypatch.setattr(obnd, attr, value)
+    try:
+        pins.check_bf16_backward_bound()
+    except AssertionError:
+        return
+    raise AssertionError(f"mutation {name} passed the bf16 bound pin")
