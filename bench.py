@@ -310,13 +310,13 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel
-    "fwd": {"fetch_kib": 236632.4, "write_kib": 66560.0,
+    "fwd": {"fetch_kib": 241201.0, "write_kib": 66561.3,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "901deb5cff475037254ecd7774f52b93459e13bbff671096f14778d4f2cde362"},
+            "sha256": "62c9a1bb2c49bc6170caffa5e6f9a133b30da124141e1ceaddd37d3b2682a4b7"},
     # bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel
-    "bwd": {"fetch_kib": 66575.4 + 362755.4 + 316869.5, "write_kib": 2048.0 + 262144.0 + 131072.0,
+    "bwd": {"fetch_kib": 66568.8 + 364086.4 + 327039.3, "write_kib": 2048.0 + 262144.0 + 131072.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "9641265b01a61770bf0a8b1d84cfc8a0e4b272611d9f23f3861fccfea306c583"},
+            "sha256": "9cb58ab923d9aad7ac6f5220841e15f98628de1c53a6578bf4b2947011b456a7"},
 }
 
 

@@ -210,9 +210,16 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   const BufRes dores = make_buf(a.dO + hoff, head_bytes);
 
   const int q_first = qt * BM;
-  const int wave_q0 = q_first + 32 * (2 * wg + grp);
-  const int qrow = wave_q0 + l32;
   const int hs = SPARSE ? (wg >> 1) : 0;  // this wave's tile stream
+  // block-sparse: the two mask rows this workgroup serves, one per stream
+  __shared__ int win_cnt[16];
+  const int2 mrows = SPARSE ? sparse_row_pair<CAUSAL>(a.mask, a.nb, nqt, qt, w, lane, win_cnt)
+                            : make_int2(2 * qt, 2 * qt + 1);
+  // query blocks interleave between the groups so that causal work is balanced; a
+  // block-sparse stream hs holds the 128 queries of its mask row
+  const int wave_q0 = SPARSE ? 128 * (hs == 0 ? mrows.x : mrows.y) + 32 * (2 * (wg & 1) + grp)
+                             : q_first + 32 * (2 * wg + grp);
+  const int qrow = wave_q0 + l32;
   const int wi = SPARSE ? (wg & 1) : wg;  // this wave's share of a tile load
   unsigned short* const kb0 = kbuf_0 + hs * C::TILE;
   unsigned short* const kb1 = kbuf_1 + hs * C::TILE;
@@ -224,8 +231,8 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   if (SPARSE) {
     constexpr int R = 128 / BN;  // key tiles per mask column
     const int nb = a.nb;
-    if (w < 2) {  // wave h lists the columns kept by mask row 2 qt + h
-      const int r = 2 * qt + w;
+    if (w < 2) {  // wave h lists the columns kept by the mask row of stream h
+      const int r = w == 0 ? mrows.x : mrows.y;
       const int ncol = r >= nb ? 0 : (CAUSAL ? r + 1 : nb);
       const unsigned char* mrow = a.mask + (size_t)min(r, nb - 1) * nb;
       int cnt = 0;

@@ -325,5 +325,49 @@ __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Block-sparse: the two 128-row mask rows served by the 256-query workgroup qt.
+// Workgroups come in windows of 8 (16 consecutive mask rows; fewer at the end of
+// the grid); inside a window the rows are ranked by the number of tiles they
+// keep (ties by row index) and workgroup j takes ranks 2j and 2j + 1, so that its
+// two tile streams have similar lengths.  Rows past the mask count as empty.
+// All 8 waves take part (two rows each); contains one workgroup barrier.
+template <bool CAUSAL>
+__device__ __forceinline__ int2 sparse_row_pair(const unsigned char* mask, int nb, int nqt, int qt, int w,
+                                                int lane, int* win_cnt) {
+  constexpr int WIN = 16;
+  const int win0 = (qt >> 3) * WIN;
+  const int wn = min(WIN, 2 * nqt - win0);  // rows this window's workgroups serve
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int j = 2 * w + i;
+    const int r = win0 + j;
+    int cnt = 0x7fffffff;  // outside the window: ranked after every row in it
+    if (j < wn) {
+      cnt = 0;
+      const int ncol = r >= nb ? 0 : (CAUSAL ? r + 1 : nb);
+      const unsigned char* mrow = mask + (size_t)min(r, nb - 1) * nb;
+      for (int base = 0; base < ncol; base += 64) {
+        const int col = base + lane;
+        cnt += __popcll(__ballot(col < ncol && mrow[col] != 0));
+      }
+    }
+    if (lane == 0) win_cnt[j] = cnt;
+  }
+  __syncthreads();
+  // lane j < 16 ranks row j; the rows ranked 2 (qt % 8) and 2 (qt % 8) + 1 are this workgroup's
+  const int j = lane & (WIN - 1);
+  const int cj = win_cnt[j];
+  int rank = 0;
+#pragma unroll
+  for (int i = 0; i < WIN; ++i) {
+    const int ci = win_cnt[i];
+    rank += (ci < cj || (ci == cj && i < j)) ? 1 : 0;
+  }
+  const int want = 2 * (qt & 7);
+  const unsigned long long ba = __ballot(lane < WIN && rank == want);
+  const unsigned long long bb = __ballot(lane < WIN && rank == want + 1);
+  return make_int2(win0 + __ffsll((long long)ba) - 1, win0 + __ffsll((long long)bb) - 1);
+}
+
 
 }  // namespace fa
