@@ -54,6 +54,25 @@ def test_long_16k_workload_sampled_rows():
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
 
 
+def test_million_token_sequence_sampled_rows():
+    """A long single head: N = 2^20 + 77 (a ragged tail), d = 64, causal, bf16 (8193 query
+    blocks, up to 16K key tiles per workgroup, 128 MB per input): 40 sampled rows against the
+    oracle, including the first, the last and the rows around the tail."""
+    n, d = (1 << 20) + 77, 64
+    announce(f"fwd bf16 N={n} d={d} causal")
+    q, k, v, _ = inputs.random_case(29, 1, 1, n, d, "bf16")
+    scale = api.default_scale(d)
+    o, lse = api.forward(dev(q, BF), dev(k, BF), dev(v, BF), scale, True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([inputs.sample_rows(n, 32, 29), [n - 78, n - 77, n - 76, n - 2]]))
+    idx = torch.from_numpy(rows).to(o.device)
+    go, gl = host(o[:, :, idx]), host(lse[:, :, idx])
+    ro, rl = oracle.forward_rows(q, k, v, rows, scale, True)
+    eo, el = max_err(go, ro), max_err(gl, rl)
+    report(f"N={n} d={d} causal", o=eo, lse=el, rows=float(rows.size))
+    assert eo <= TOL_BF16 and el <= TOL_LSE
+
+
 EDGE_N = [1, 2, 17, 64, 127, 128, 129, 300, 1000]
 
 
