@@ -18,6 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+CALLER = os.path.join(PKG, "fa_c_caller")
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
@@ -64,6 +65,12 @@ def build(verbose: bool = True) -> str:
     if res.returncode != 0:
         raise RuntimeError("link of libfa.so failed:\n" + res.stdout + res.stderr)
     os.replace(tmp, LIB)
+    # a plain C-ABI caller (host code only, linked against libfa.so next to it)
+    cmd = [_hipcc(), "-O2", "-std=c++17", "-Wall", "-I", INCLUDE, os.path.join(CSRC, "fa_c_caller.cpp"),
+           "-L", PKG, "-lfa", "-Wl,-rpath,$ORIGIN", "-o", CALLER]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("build of fa_c_caller failed:\n" + res.stdout + res.stderr)
     if verbose:
         print(f"built {LIB}")
     return LIB
