@@ -119,3 +119,29 @@ def test_blocksparse_backward_full_mask_equals_dense(d):
         torch.cuda.synchronize()
         for a_, b_ in zip(sparse, dense):
             assert max_err(host(a_), host(b_)) <= TOL_BF16, (d, causal)
+
+
+def test_blocksparse_backward_many_windows_bf16_gradients():
+    """N = 4500 (18 query blocks of 256: two full windows of paired mask rows and a partial
+    one), a random causal mask with an empty row and column, bf16 gradient outputs (their
+    rounding adds up to 2^-8 of each value, hence twice the bf16 gate)."""
+    n, d = 4500, 64
+    nb = -(-n // 128)
+    announce(f"sparse bwd N={n} d={d} bf16 gradients")
+    q, k, v, do = inputs.random_case(26, 1, 1, n, d, "bf16", backward=True)
+    mask = inputs.random_block_mask(27, nb, 0.3, True)
+    mask[5, :] = 0
+    mask[:, 9] = 0
+    scale = api.default_scale(d)
+    tm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda:0")
+    tq, tk, tv, tdo = dev(q, BF), dev(k, BF), dev(v, BF), dev(do, BF)
+    o, lse = api.forward_blocksparse(tq, tk, tv, tm, scale, True)
+    dq, dk, dv = api.backward(tq, tk, tv, o, lse, tdo, scale, True, grad_dtype=BF, block_mask=tm)
+    torch.cuda.synchronize()
+    ro, rl = oracle.forward(q, k, v, scale, True, mask, inputs.MASK_BLOCK)
+    rq, rk, rv = oracle.backward(q, k, v, do, scale, True, mask, inputs.MASK_BLOCK)
+    errs = dict(o=max_err(host(o), ro), lse=max_err(host(lse), rl), dq=max_err(host(dq), rq),
+                dk=max_err(host(dk), rk), dv=max_err(host(dv), rv))
+    report(f"sparse N={n} d={d} bf16 gradients", **errs)
+    assert errs["o"] <= TOL_BF16 and errs["lse"] <= TOL_LSE
+    assert max(errs["dq"], errs["dk"], errs["dv"]) <= 2 * TOL_BF16
