@@ -12,8 +12,9 @@ namespace {
 
 constexpr long long kMaxGrid = 0x7fffffffLL;
 constexpr size_t kLdsBytes = 160 * 1024;  // gfx950 LDS per workgroup
-// static LDS of the bf16 forward: K and V tiles of 16 KB, three buffers each, plus bookkeeping
-constexpr size_t kFwdStaticLds = (size_t)6 * 16384 + 64;
+// static LDS of the bf16 forward: K and V tiles of 16 KB, three buffers each, plus at most
+// 256 bytes of bookkeeping (list lengths, the row-pairing counts)
+constexpr size_t kFwdStaticLds = (size_t)6 * 16384 + 256;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -154,7 +155,7 @@ namespace {
 
 // static LDS of the block-sparse backward kernels (tile rings, hand-over buffers, bookkeeping)
 constexpr size_t bwd_dkdv_static_lds(int d) { return d == 128 ? 132608 + 64 : 83456 + 64; }
-constexpr size_t kBwdDqStaticLds = (size_t)6 * 16384 + 64;
+constexpr size_t kBwdDqStaticLds = (size_t)6 * 16384 + 256;
 
 int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* mask, const void* o, const float* lse,
              const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale,

@@ -84,7 +84,9 @@ def test_blocksparse_validation(lib):
     assert f(*base, P + 5 * MB, P + 3 * MB, P + 4 * MB, 1, 1, 256, 64, 0.125, 1, 0, None) == UNS  # fp32
     assert f(*base, P + 5 * MB, P + 3 * MB, P + 4 * MB, 1, 1, 256, 48, 0.125, 1, 1, None) == UNS
     # the visited-tile list of a 256-query block must fit in LDS next to the K/V tiles
-    for d, n_bad in ((64, 2095104 + 128), (128, 2095104 + 128)):
+    # (2088960 = 16320 mask rows of 128 is the largest N whose two lists fit beside 96 KB of
+    # tiles and 256 bytes of bookkeeping; only rejected sizes are called here, no GPU is used)
+    for d, n_bad in ((64, 2088960 + 1), (128, 2088960 + 1), (64, 2095104 + 128), (128, 2095104 + 128)):
         assert f(*base, P + 5 * MB, P + 3 * MB, P + 4 * MB, 1, 1, n_bad, d, 0.125, 1, 1, None) == UNS
 
 
