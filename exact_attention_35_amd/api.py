@@ -162,26 +162,36 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
 
 
 class FlashAttentionFunction(torch.autograd.Function):
-    """autograd wrapper: forward saves (q, k, v, o, lse); backward calls fa_bwd."""
+    """autograd wrapper: forward saves (q, k, v, o, lse[, block_mask]); backward calls fa_bwd
+    (fa_bwd_gqa, fa_bwd_blocksparse)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, scale=None, causal=False):
-        o, lse = forward(q, k, v, scale, causal)
-        ctx.save_for_backward(q, k, v, o, lse)
+    def forward(ctx, q, k, v, scale=None, causal=False, block_mask=None):
+        if block_mask is None:
+            o, lse = forward(q, k, v, scale, causal)
+            ctx.save_for_backward(q, k, v, o, lse)
+        else:
+            o, lse = forward_blocksparse(q, k, v, block_mask, scale, causal)
+            ctx.save_for_backward(q, k, v, o, lse, block_mask)
         ctx.scale = default_scale(q.shape[-1]) if scale is None else float(scale)
         ctx.causal = causal
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.scale, ctx.causal, grad_dtype=q.dtype)
-        return dq, dk, dv, None, None
+        q, k, v, o, lse, *mask = ctx.saved_tensors
+        dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.scale, ctx.causal, grad_dtype=q.dtype,
+                              block_mask=mask[0] if mask else None)
+        return dq, dk, dv, None, None, None
 
 
-def attention(q, k, v, scale=None, causal=False):
-    """Differentiable exact attention (bf16 gradients for bf16 inputs); k, v may have H_kv | H heads."""
-    return FlashAttentionFunction.apply(q, k, v, scale, causal)
+def attention(q, k, v, scale=None, causal=False, block_mask=None):
+    """Differentiable exact attention (bf16 gradients for bf16 inputs).
+
+    k, v may have H_kv | H heads (grouped-/multi-query); block_mask (uint8
+    [ceil(N/128), ceil(N/128)], full heads only) makes it block-sparse.
+    """
+    return FlashAttentionFunction.apply(q, k, v, scale, causal, block_mask)
 
 
 def fp8_scale_shape(B: int, H: int, N: int) -> Tuple[int, int, int]:

@@ -132,6 +132,23 @@ def test_equals_repeated_kv(d):
             _repeat_equivalence(2, H, hkv, N, d, causal, 31 + N + d)
 
 
+def test_autograd_wrapper_grouped_query():
+    """api.attention with 8 query heads on 2 K/V heads: output and gradients (dK, dV of the
+    shared heads' shape) equal the explicit fa_fwd_gqa / fa_bwd_gqa calls bit for bit."""
+    announce("autograd wrapper, grouped-query")
+    q, k, v, do = inputs.random_case(30, 1, 8, 200, 64, "bf16", backward=True, h_kv=2)
+    tq, tk, tv = (dev(x, BF).requires_grad_(True) for x in (q, k, v))
+    out = api.attention(tq, tk, tv, None, True)
+    out.backward(dev(do, BF))
+    o, lse = api.forward(tq.detach(), tk.detach(), tv.detach(), None, True)
+    eq = api.backward(tq.detach(), tk.detach(), tv.detach(), o, lse, dev(do, BF), None, True, grad_dtype=BF)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), o)
+    assert tk.grad.shape == tk.shape and tv.grad.shape == tv.shape
+    for g, e in zip((tq.grad, tk.grad, tv.grad), eq):
+        assert torch.equal(g, e)
+
+
 def test_gqa_workload_full_size():
     """The 16K, 32-query / 8-K/V-head workload in the launch configuration the benchmark times:
     O and lse at sampled rows against the oracle, and the whole forward and backward against

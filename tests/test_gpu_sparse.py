@@ -145,3 +145,28 @@ def test_blocksparse_backward_many_windows_bf16_gradients():
     report(f"sparse N={n} d={d} bf16 gradients", **errs)
     assert errs["o"] <= TOL_BF16 and errs["lse"] <= TOL_LSE
     assert max(errs["dq"], errs["dk"], errs["dv"]) <= 2 * TOL_BF16
+
+
+def test_autograd_wrapper_with_block_mask():
+    """api.attention with a block mask: the forward and the gradients equal the explicit
+    fa_fwd_blocksparse / fa_bwd_blocksparse calls (bf16 gradients), and the oracle."""
+    n, d = 300, 64
+    nb = -(-n // 128)
+    announce("autograd wrapper, block-sparse")
+    q, k, v, do = inputs.random_case(28, 1, 2, n, d, "bf16", backward=True)
+    mask = inputs.random_block_mask(29, nb, 0.5, True)
+    tm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda:0")
+    tq, tk, tv = (dev(x, BF).requires_grad_(True) for x in (q, k, v))
+    out = api.attention(tq, tk, tv, None, True, tm)
+    out.backward(dev(do, BF))
+    o, lse = api.forward_blocksparse(tq.detach(), tk.detach(), tv.detach(), tm, None, True)
+    eq = api.backward(tq.detach(), tk.detach(), tv.detach(), o, lse, dev(do, BF), None, True, grad_dtype=BF,
+                      block_mask=tm)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), o)
+    for g, e in zip((tq.grad, tk.grad, tv.grad), eq):
+        assert torch.equal(g, e)
+    scale = api.default_scale(d)
+    rq, rk, rv = oracle.backward(q, k, v, do, scale, True, mask, inputs.MASK_BLOCK)
+    for g, r in ((tq.grad, rq), (tk.grad, rk), (tv.grad, rv)):
+        assert max_err(host(g), r) <= 2 * TOL_BF16
