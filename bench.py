@@ -314,9 +314,9 @@ MEASURED_TRAFFIC = {
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
             "sha256": "62c9a1bb2c49bc6170caffa5e6f9a133b30da124141e1ceaddd37d3b2682a4b7"},
     # bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel
-    "bwd": {"fetch_kib": 66568.8 + 364086.4 + 327039.3, "write_kib": 2048.0 + 262144.0 + 131072.0,
+    "bwd": {"fetch_kib": 66575.2 + 366495.1 + 317539.1, "write_kib": 2048.0 + 262144.0 + 131072.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "9cb58ab923d9aad7ac6f5220841e15f98628de1c53a6578bf4b2947011b456a7"},
+            "sha256": "bde7941ea5bda37c93cd3e26de24afbfa4971f51a6fe66d5e32b623f2f29c257"},
 }
 
 

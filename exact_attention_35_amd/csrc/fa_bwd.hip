@@ -33,7 +33,7 @@
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// stats[row] = (lse * log2 e, D = rowsum(dO * O)).  T = unsigned short (bf16 bits) or float.
+// stats[row] = (lse * log2 e, -D) with D = rowsum(dO * O).  T = unsigned short (bf16 bits) or float.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, const T* __restrict__ dO,
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, 
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && part == 0) {
     const float l = lse[row];
-    stats[row] = make_float2(l == -INFINITY ? INFINITY : l * kLog2e, acc);
+    stats[row] = make_float2(l == -INFINITY ? INFINITY : l * kLog2e, -acc);
   }
 }
 
@@ -118,7 +118,7 @@ struct BwdBf16Args {
   const unsigned short* k;
   const unsigned short* v;
   const unsigned short* dO;
-  const float2* stats;  // per row: (lse log2 e, D)
+  const float2* stats;  // per row: (lse log2 e, -D)
   const unsigned char* mask;  // block-sparse 128x128 tile mask [nb, nb], or null
   int nb;
   void* dq;
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   if (qrow < N) {
     const float2 st = a.stats[(size_t)bh * N + qrow];
     lse2 = st.x;
-    dlt = st.y;
+    dlt = -st.y;
   }
   const KOffsets<D> ko = k_offsets<D>(l32, half);
   const KtOffsets<D> kto = kt_offsets<D>(lane);
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
 // i+1 while the gradient waves run dV += dO(i)^T P(i); phase b: the score waves
 // compute P(i+1), dS(i+1) and hand over P(i+1) while the gradient waves fetch
 // tile i+2 and run dK += Q(i)^T dS(i).  Q and dO tiles (64 queries, K layout)
-// and their (lse, D) rows sit in rings of three buffers.
+// and their (lse log2 e, -D) rows sit in rings of three buffers.
 // ---------------------------------------------------------------------------
 // MFMA / LDS-read interleave of an MFMA phase (masks: 0x8 MFMA, 0x100 LDS read):
 // PRE reads issue first, then after each MFMA the reads of a later one, so
@@ -525,11 +525,21 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
     const int tq = tile_q(i);
     dma_k<D, BQ>(qres, qb, tq, sw, lane);
     dma_k<D, BQ>(dores, ob, tq, sw, lane);
-    if (sw == 0 && lane < 32)  // 64 rows x 8 bytes; rows past N read as zeros
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_void_t*)st, 16, (unsigned int)(tq * BQ * 8 + 16 * lane),
-                                               0, 0, 0);
+    if (sw == 0) {
+      // the 64 rows' (lse log2 e, -D) pairs regrouped per four rows: LDS dword 8g + e holds
+      // lse log2 e of row 4g + e for e < 4 and -D of row 4g + e - 4 for e >= 4, so that
+      // one 16-byte read gives four rows' -D, the initial dP accumulator (rows past N: zeros)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int j = 64 * m + lane;
+        const int row = 4 * (j >> 3) + (j & 3);
+        const unsigned int off = (unsigned int)((tq * BQ + row) * 8 + 4 * ((j >> 2) & 1));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_void_t*)(reinterpret_cast<float*>(st) + 64 * m), 4, off,
+                                                 0, 0, 0);
+      }
+    }
   };
-  constexpr int LOADS = 2 * C::KB_PER_WAVE + 1;  // loads of one fetch by gradient wave 0 (the others: one fewer)
+  constexpr int LOADS = 2 * C::KB_PER_WAVE + 2;  // loads of one fetch by gradient wave 0 (the others: two fewer)
 
   // Every buffer starts as zeros: rows past N (which the range-checked loads may
   // leave unwritten) are multiplied by P = dS = 0 and must hold finite values.
@@ -547,7 +557,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
     fetch(0, qbuf_0, obuf_0, st_0);
     if (T > 1) {
       fetch(1, qbuf_1, obuf_1, st_1);
-      if (sw == 0) wait_dma_but<LOADS>(); else wait_dma_but<LOADS - 1>();  // tile 1 may still be landing
+      if (sw == 0) wait_dma_but<LOADS>(); else wait_dma_but<LOADS - 2>();  // tile 1 may still be landing
     } else {
       wait_dma();
     }
@@ -594,27 +604,27 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
       __builtin_amdgcn_s_setprio(0);
     };
     // P of tile i (register r of block b is query 32b + acc_row_swapped(r, half)), kept in s
-    // as fp32 for dS and packed for the handover; dp starts at -D of the same query.
+    // as fp32 for dS and packed for the handover; dp starts at -D of the same query, read
+    // from LDS straight into the accumulator.
     // The masked variant is a separate copy so that the common path has no per-element selects.
     auto p_body = [&](int q0, const float2* st, auto mask_tag) __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(mask_tag)::value;
 #pragma unroll
       for (int b = 0; b < NSB; ++b) {
+        // registers 8g + e are queries 32b + 16g + 8h + e, e = 0..7: per g two four-row
+        // groups (lse log2 e x 4, then -D x 4); the four -D quads form dp[b] as one tuple
+        const f32x4* src = reinterpret_cast<const f32x4*>(st + 32 * b + 8 * half);
+        dp[b] = __builtin_shufflevector(__builtin_shufflevector(src[1], src[3], 0, 1, 2, 3, 4, 5, 6, 7),
+                                        __builtin_shufflevector(src[9], src[11], 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2,
+                                        3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          // queries 32b + 16g + 8h + e, e = 0..7: four float4 reads of (lse log2 e, D) pairs
-          const float4* src = reinterpret_cast<const float4*>(st + 32 * b + 16 * g + 8 * half);
-          float2 sd[8];
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float4 x = src[e2];
-            sd[2 * e2] = make_float2(x.x, x.y);
-            sd[2 * e2 + 1] = make_float2(x.z, x.w);
-          }
+          const f32x4 l0 = src[8 * g], l1 = src[8 * g + 2];
+          const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int r = 8 * g + e;
-            float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -sd[e].x));
+            float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -lv[e]));
             if (MASKED) {
               // query = base + off with off = 16(r/8) + (r%8) a constant
               const int base = q0 + 32 * b + 8 * half;
@@ -623,7 +633,6 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
               p = hide ? 0.f : p;
             }
             s[b][r] = p;
-            dp[b][r] = -sd[e].y;
           }
         }
       }
@@ -727,7 +736,7 @@ struct BwdF32Args {
   const float* v;
   const float* dO;
   const float* lse;
-  const float2* stats;  // (lse log2 e, D) per row; D is used here
+  const float2* stats;  // (lse log2 e, -D) per row; D is used here
   float* dq;
   float* dk;
   float* dv;
@@ -774,7 +783,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dkdv_kernel(BwdF32Args a) {
     if (tid < BQ) {
       const int row = q0 + tid;
       ls[tid] = row < N ? a.lse[hoff / D + row] : -INFINITY;
-      dl[tid] = row < N ? a.stats[hoff / D + row].y : 0.f;
+      dl[tid] = row < N ? -a.stats[hoff / D + row].y : 0.f;
     }
     __syncthreads();
     if (key < N) {
@@ -828,7 +837,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdF32Args a) {
     g[t] = 0.f;
   }
   const float l = in ? a.lse[hoff / D + qi] : -INFINITY;
-  const float dl = in ? a.stats[hoff / D + qi].y : 0.f;
+  const float dl = in ? -a.stats[hoff / D + qi].y : 0.f;
   const int kend = CAUSAL ? min(N, qt * BQ + BQ) : N;
   for (int k0 = 0; k0 < kend; k0 += BK) {
     __syncthreads();

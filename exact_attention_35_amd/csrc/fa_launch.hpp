@@ -31,7 +31,7 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* stats;  // workspace: per row of [B, H, N], the pair (lse * log2 e, D = rowsum(dO * O))
+  float* stats;  // workspace: per row of [B, H, N], the pair (lse * log2 e, -D) with D = rowsum(dO * O)
   // workspace, grouped-query only (Hkv < H): fp32 dK and dV of every query head, [B, H, N, d] each,
   // summed over each group into dk / dv by a final kernel
   float* part_k;

@@ -99,8 +99,8 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, const unsign
 
 /*
  * Bytes of workspace fa_bwd needs: 8 per row of [B, H, N] (the row's lse * log2 e
- * and D = rowsum(dO * O), two fp32 values).  Returns 0 for arguments fa_bwd
- * would reject.
+ * and -D with D = rowsum(dO * O), two fp32 values).  Returns 0 for arguments
+ * fa_bwd would reject.
  */
 size_t fa_bwd_workspace_size(int B, int H, int N, int d, int grad_dtype);
 
