@@ -312,11 +312,11 @@ MEASURED_TRAFFIC = {
     # fwd_bf16_kernel
     "fwd": {"fetch_kib": 241201.0, "write_kib": 66561.3,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "62c9a1bb2c49bc6170caffa5e6f9a133b30da124141e1ceaddd37d3b2682a4b7"},
+            "sha256": "ce10357b2478a6bf8739845889e411e5778bc26311878750502524b3f0881268"},
     # bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel
     "bwd": {"fetch_kib": 66575.2 + 366495.1 + 317539.1, "write_kib": 2048.0 + 262144.0 + 131072.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "bde7941ea5bda37c93cd3e26de24afbfa4971f51a6fe66d5e32b623f2f29c257"},
+            "sha256": "49bca1beb47670b8024c6e33900769b6751ca78413544b5ffd2742a4a66d5aca"},
 }
 
 

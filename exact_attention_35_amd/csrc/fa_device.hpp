@@ -67,25 +67,6 @@ __device__ __forceinline__ int acc_row_swapped(int r, int half) {
   return 16 * (r >> 3) + 8 * half + (r & 7);
 }
 
-// Transpose a 4-row x 8-column bf16 micro-block held as four uint4 rows into
-// eight 4-element columns (uint2 each): column e holds rows 0..3 of element e.
-__device__ __forceinline__ uint2 column_of(const uint4 (&rows)[4], int e) {
-  const unsigned int* r0 = reinterpret_cast<const unsigned int*>(&rows[0]);
-  const unsigned int* r1 = reinterpret_cast<const unsigned int*>(&rows[1]);
-  const unsigned int* r2 = reinterpret_cast<const unsigned int*>(&rows[2]);
-  const unsigned int* r3 = reinterpret_cast<const unsigned int*>(&rows[3]);
-  const int w = e >> 1;
-  uint2 out;
-  if (e & 1) {
-    out.x = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
-    out.y = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
-  } else {
-    out.x = (r0[w] & 0xffffu) | (r1[w] << 16);
-    out.y = (r2[w] & 0xffffu) | (r3[w] << 16);
-  }
-  return out;
-}
-
 // max of three fp32 values in one v_max3_f32 (fmaxf would first canonicalize
 // every input, doubling the instruction count; the scores are never NaN)
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -116,14 +97,6 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 __device__ __forceinline__ unsigned short bf16_lane_of(const uint4& u, int e) {
   const unsigned int w = (e >> 1) == 0 ? u.x : (e >> 1) == 1 ? u.y : (e >> 1) == 2 ? u.z : u.w;
   return (unsigned short)((e & 1) ? (w >> 16) : (w & 0xffffu));
-}
-
-__device__ __forceinline__ uint4 flip_sign_bf16(uint4 u) {
-  u.x ^= 0x80008000u;
-  u.y ^= 0x80008000u;
-  u.z ^= 0x80008000u;
-  u.w ^= 0x80008000u;
-  return u;
 }
 
 __device__ __forceinline__ uint4 zero_uint4() { return make_uint4(0u, 0u, 0u, 0u); }
