@@ -78,24 +78,28 @@ def forward_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
                         scale: Optional[float] = None, causal: bool = False, with_lse: bool = True,
                         out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None
                         ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Block-sparse forward; block_mask is uint8 [ceil(N/128), ceil(N/128)] on the same GPU."""
-    B, H, N, d = _check_qkv(q, k, v)
-    nb = -(-N // _lib.FA_MASK_BLOCK)
-    if block_mask.dtype != torch.uint8 or tuple(block_mask.shape) != (nb, nb):
-        raise ValueError(f"block_mask must be uint8 [{nb}, {nb}]")
-    if not block_mask.is_contiguous() or block_mask.device != q.device:
-        raise ValueError("block_mask must be contiguous and on the same GPU as q")
+    """Block-sparse forward; block_mask is uint8 [ceil(N/128), ceil(N/128)] on the same GPU.
+
+    k and v may hold fewer heads than q (grouped-/multi-query, fa_fwd_blocksparse_gqa).
+    """
+    B, H, N, d = _check_qkv(q, k, v, allow_gqa=True)
+    hkv = k.shape[1]
+    _check_mask(block_mask, N, q.device)
     scale = default_scale(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     lse = None
     if with_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    lib = _lib.load()
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), block_mask.data_ptr(), o.data_ptr(),
+            lse.data_ptr() if lse is not None else None)
+    tail = (N, d, scale, int(bool(causal)), _DTYPES[q.dtype], _stream_ptr(q.device))
     with torch.cuda.device(q.device):
-        st = _lib.load().fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), block_mask.data_ptr(),
-                                            o.data_ptr(), lse.data_ptr() if lse is not None else None,
-                                            B, H, N, d, scale, int(bool(causal)), _DTYPES[q.dtype],
-                                            _stream_ptr(q.device))
-    _lib.check(st, "fa_fwd_blocksparse")
+        if hkv == H:
+            st = lib.fa_fwd_blocksparse(*ptrs, B, H, *tail)
+        else:
+            st = lib.fa_fwd_blocksparse_gqa(*ptrs, B, H, hkv, *tail)
+    _lib.check(st, "fa_fwd_blocksparse" if hkv == H else "fa_fwd_blocksparse_gqa")
     return o, lse
 
 
@@ -122,9 +126,10 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
 
     With block_mask (uint8 [ceil(N/128), ceil(N/128)], as for forward_blocksparse) this is
     the block-sparse backward, fa_bwd_blocksparse.  With k and v of H_kv < H heads it is the
-    grouped-query backward, fa_bwd_gqa: dk and dv then have k's shape.
+    grouped-query backward, fa_bwd_gqa (with a mask too: fa_bwd_blocksparse_gqa); dk and dv
+    then have k's shape.
     """
-    B, H, N, d = _check_qkv(q, k, v, allow_gqa=block_mask is None)
+    B, H, N, d = _check_qkv(q, k, v, allow_gqa=True)
     hkv = k.shape[1]
     if block_mask is not None:
         _check_mask(block_mask, N, q.device)
@@ -148,9 +153,12 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
     with torch.cuda.device(q.device):
-        if block_mask is not None:
+        if block_mask is not None and hkv == H:
             name = "fa_bwd_blocksparse"
             st = lib.fa_bwd_blocksparse(*ptrs[:3], block_mask.data_ptr(), *ptrs[3:], B, H, *tail)
+        elif block_mask is not None:
+            name = "fa_bwd_blocksparse_gqa"
+            st = lib.fa_bwd_blocksparse_gqa(*ptrs[:3], block_mask.data_ptr(), *ptrs[3:], B, H, hkv, *tail)
         elif hkv != H:
             name = "fa_bwd_gqa"
             st = lib.fa_bwd_gqa(*ptrs, B, H, hkv, *tail)
@@ -163,7 +171,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
 
 class FlashAttentionFunction(torch.autograd.Function):
     """autograd wrapper: forward saves (q, k, v, o, lse[, block_mask]); backward calls fa_bwd
-    (fa_bwd_gqa, fa_bwd_blocksparse)."""
+    (fa_bwd_gqa, fa_bwd_blocksparse, fa_bwd_blocksparse_gqa)."""
 
     @staticmethod
     def forward(ctx, q, k, v, scale=None, causal=False, block_mask=None):
@@ -189,7 +197,7 @@ def attention(q, k, v, scale=None, causal=False, block_mask=None):
     """Differentiable exact attention (bf16 gradients for bf16 inputs).
 
     k, v may have H_kv | H heads (grouped-/multi-query); block_mask (uint8
-    [ceil(N/128), ceil(N/128)], full heads only) makes it block-sparse.
+    [ceil(N/128), ceil(N/128)]) makes it block-sparse, with or without grouped heads.
     """
     return FlashAttentionFunction.apply(q, k, v, scale, causal, block_mask)
 

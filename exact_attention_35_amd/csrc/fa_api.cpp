@@ -137,6 +137,12 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, const unsign
   return fwd_impl(q, k, v, block_mask, o, lse, B, H, H, N, d, scale, causal, dtype, stream, true);
 }
 
+int fa_fwd_blocksparse_gqa(const void* q, const void* k, const void* v, const unsigned char* block_mask, void* o,
+                           float* lse, int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype,
+                           void* stream) {
+  return fwd_impl(q, k, v, block_mask, o, lse, B, H, H_kv, N, d, scale, causal, dtype, stream, true);
+}
+
 size_t fa_bwd_gqa_workspace_size(int B, int H, int H_kv, int N, int d, int grad_dtype) {
   if (check_common(B, H, N, d, 1.0f, 0, grad_dtype) != FA_OK || !valid_kv_heads(H, H_kv)) return 0;
   const size_t n = (size_t)B * H * N;
@@ -255,6 +261,14 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const unsign
                        float scale, int causal, int dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
                        void* stream) {
   return bwd_impl(q, k, v, block_mask, o, lse, dO, dq, dk, dv, B, H, H, N, d, scale, causal, dtype, grad_dtype,
+                  workspace, workspace_bytes, stream, true);
+}
+
+int fa_bwd_blocksparse_gqa(const void* q, const void* k, const void* v, const unsigned char* block_mask,
+                           const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, int B,
+                           int H, int H_kv, int N, int d, float scale, int causal, int dtype, int grad_dtype,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, block_mask, o, lse, dO, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype, grad_dtype,
                   workspace, workspace_bytes, stream, true);
 }
 

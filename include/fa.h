@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 #define FA_MASK_BLOCK 128 /* rows and keys covered by one block-sparse mask entry */
 #define FA_FP8_BLOCK 128  /* rows of one head that share one fp8 scale */
 
@@ -154,6 +154,29 @@ int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const unsign
                        const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
                        int B, int H, int N, int d, float scale, int causal, int dtype, int grad_dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Block-sparse attention with grouped-query / multi-query K/V heads: the mask
+ * of fa_fwd_blocksparse and the head sharing of fa_fwd_gqa together (q, o, lse
+ * [B, H, ...]; k, v [B, H_kv, N, d]; one block_mask shared by every (b, h)).
+ * Arguments, limits and errors as fa_fwd_blocksparse, plus those of H_kv as in
+ * fa_fwd_gqa; H_kv == H is identical to fa_fwd_blocksparse.
+ */
+int fa_fwd_blocksparse_gqa(const void* q, const void* k, const void* v, const unsigned char* block_mask,
+                           void* o, float* lse, int B, int H, int H_kv, int N, int d, float scale,
+                           int causal, int dtype, void* stream);
+
+/*
+ * Backward of fa_fwd_blocksparse_gqa (same block_mask, H_kv, scale and causal;
+ * o and lse from that call): dq [B, H, N, d]; dk, dv [B, H_kv, N, d] summed
+ * over each group's query heads in head order, as in fa_bwd_gqa.  The
+ * workspace is sized by fa_bwd_gqa_workspace_size(); arguments and errors as
+ * fa_bwd_blocksparse and fa_bwd_gqa.
+ */
+int fa_bwd_blocksparse_gqa(const void* q, const void* k, const void* v, const unsigned char* block_mask,
+                           const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                           int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype,
+                           int grad_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * FP8 quantisation with incoherent processing (everydayai.blog flash-attention

@@ -161,6 +161,29 @@ def test_gqa_validation(lib):
     assert g(*ptrs[:7], ptrs[6] + 64, ptrs[8], 1, 8, 2, 64, 64, 0.125, 1, 1, 0, P + 10 * MB, ws, None) == INV
 
 
+def test_blocksparse_gqa_validation(lib):
+    f = lib.fa_fwd_blocksparse_gqa
+    base = (P, P + MB, P + 2 * MB)
+    m, o, lse = P + 5 * MB, P + 3 * MB, P + 4 * MB
+    assert f(*base, m, o, lse, 1, 8, 3, 256, 64, 0.125, 1, 1, None) == INV  # 3 does not divide 8
+    assert f(*base, m, o, lse, 1, 8, 16, 256, 64, 0.125, 1, 1, None) == INV
+    assert f(*base, None, o, lse, 1, 8, 2, 256, 64, 0.125, 1, 1, None) == INV  # no mask
+    assert f(*base, m, o, lse, 1, 8, 2, 256, 64, 0.125, 1, 0, None) == UNS  # fp32
+    assert f(*base, m, o, lse, 1, 8, 2, 256, 48, 0.125, 1, 1, None) == UNS
+    assert f(*base, m, o, lse, 1, 8, 2, 2088960 + 1, 64, 0.125, 1, 1, None) == UNS  # lists do not fit in LDS
+    g = lib.fa_bwd_blocksparse_gqa
+    ptrs = [P + i * MB for i in range(10)]
+    ws = lib.fa_bwd_gqa_workspace_size(1, 8, 2, 64, 64, 0)
+    def call(mask=ptrs[3], hkv=2, dtype=1, wsb=ws):
+        return g(ptrs[0], ptrs[1], ptrs[2], mask, ptrs[4], ptrs[5], ptrs[6], ptrs[7], ptrs[8], ptrs[9],
+                 1, 8, hkv, 64, 64, 0.125, 1, dtype, 0, P + 11 * MB, wsb, None)
+    assert call(mask=None) == INV
+    assert call(hkv=3) == INV
+    assert call(dtype=0) == UNS
+    assert call(wsb=ws - 16) == WS  # the grouped-query workspace holds the per-head dK/dV partials
+    assert call(mask=ptrs[8]) == INV  # the mask overlaps an output
+
+
 def test_gqa_workspace_size(lib):
     n = 2 * 8 * 100
     assert lib.fa_bwd_gqa_workspace_size(2, 8, 8, 100, 64, 0) == n * 8 == lib.fa_bwd_workspace_size(2, 8, 100, 64, 0)

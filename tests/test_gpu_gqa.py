@@ -1,4 +1,5 @@
-"""GPU parity of grouped-/multi-query attention (fa_fwd_gqa, fa_bwd_gqa) against the fp64 oracle.
+"""GPU parity of grouped-/multi-query attention (fa_fwd_gqa, fa_bwd_gqa, and with a block mask
+fa_fwd_blocksparse_gqa, fa_bwd_blocksparse_gqa) against the fp64 oracle.
 
 K and V carry H_kv heads; query head h reads K/V head h // (H / H_kv).  dK and dV
 of a shared head are sums over its H / H_kv query heads: their rounding errors
@@ -96,9 +97,10 @@ def test_bf16_gradient_outputs():
     assert max(e["dk"], e["dv"]) <= 2 * TOL_BF16 * math.sqrt(4)
 
 
-def _repeat_equivalence(B, H, hkv, N, d, causal, seed):
+def _repeat_equivalence(B, H, hkv, N, d, causal, seed, mask=None):
     """fa_*_gqa == fa_* on K/V repeated per query head: bitwise for O, lse and dQ; dK/dV equal
-    the head-order fp32 sums of the dense per-head gradients, bitwise."""
+    the head-order fp32 sums of the dense per-head gradients, bitwise.  With a block mask the
+    same holds for fa_*_blocksparse_gqa against fa_*_blocksparse."""
     g = H // hkv
     gen = torch.Generator(device="cuda:0")
     gen.manual_seed(seed)
@@ -106,11 +108,13 @@ def _repeat_equivalence(B, H, hkv, N, d, causal, seed):
     k, v = (torch.randn((B, hkv, N, d), generator=gen, device="cuda:0").to(BF) for _ in range(2))
     rk = k.repeat_interleave(g, dim=1).contiguous()
     rv = v.repeat_interleave(g, dim=1).contiguous()
-    o, lse = api.forward(q, k, v, None, causal)
-    ro, rl = api.forward(q, rk, rv, None, causal)
+    tm = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask)).to("cuda:0")
+    fwd = api.forward if tm is None else (lambda q_, k_, v_, s_, c_: api.forward_blocksparse(q_, k_, v_, tm, s_, c_))
+    o, lse = fwd(q, k, v, None, causal)
+    ro, rl = fwd(q, rk, rv, None, causal)
     assert torch.equal(o, ro) and torch.equal(lse, rl)
-    dq, dk, dv = api.backward(q, k, v, o, lse, do, None, causal)
-    rdq, rdk, rdv = api.backward(q, rk, rv, ro, rl, do, None, causal)
+    dq, dk, dv = api.backward(q, k, v, o, lse, do, None, causal, block_mask=tm)
+    rdq, rdk, rdv = api.backward(q, rk, rv, ro, rl, do, None, causal, block_mask=tm)
     assert torch.equal(dq, rdq)
     for got, dense in ((dk, rdk), (dv, rdv)):
         parts = dense.view(B, hkv, g, N, d)
@@ -119,7 +123,7 @@ def _repeat_equivalence(B, H, hkv, N, d, causal, seed):
             acc += parts[:, :, j]
         assert torch.equal(got, acc)
     # bf16 gradients: the same sums, rounded once
-    _, bdk, bdv = api.backward(q, k, v, o, lse, do, None, causal, grad_dtype=BF)
+    _, bdk, bdv = api.backward(q, k, v, o, lse, do, None, causal, grad_dtype=BF, block_mask=tm)
     assert torch.equal(bdk, dk.to(BF)) and torch.equal(bdv, dv.to(BF))
     torch.cuda.synchronize()
 
@@ -132,6 +136,48 @@ def test_equals_repeated_kv(d):
             _repeat_equivalence(2, H, hkv, N, d, causal, 31 + N + d)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_blocksparse_grouped_query(d, causal):
+    """fa_fwd_blocksparse_gqa / fa_bwd_blocksparse_gqa against the oracle's masked attention
+    with shared K/V heads (a mask row without visible keys, a mask column no query sees)."""
+    for H, hkv in ((8, 2), (4, 1)):
+        g = H // hkv
+        for n in (129, 600):
+            nb = -(-n // 128)
+            name = f"sparse gqa H={H} H_kv={hkv} N={n} d={d} causal={causal}"
+            announce(name)
+            q, k, v, do = inputs.random_case(32, 1, H, n, d, "bf16", backward=True, h_kv=hkv)
+            mask = inputs.random_block_mask(33, nb, 0.5, causal)
+            if nb > 2:
+                mask[1, :] = 0
+                mask[:, 0] = 0
+            scale = api.default_scale(d)
+            tm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda:0")
+            tq, tk, tv, tdo = dev(q, BF), dev(k, BF), dev(v, BF), dev(do, BF)
+            o, lse = api.forward_blocksparse(tq, tk, tv, tm, scale, causal)
+            dq, dk, dv = api.backward(tq, tk, tv, o, lse, tdo, scale, causal, block_mask=tm)
+            torch.cuda.synchronize()
+            ro, rl = oracle.forward(q, k, v, scale, causal, mask, inputs.MASK_BLOCK)
+            rdq, rdk, rdv = oracle.backward(q, k, v, do, scale, causal, mask, inputs.MASK_BLOCK)
+            e = dict(o=max_err(host(o), ro), lse=max_err(host(lse), rl), dq=max_err(host(dq), rdq),
+                     dk=max_err(host(dk), rdk), dv=max_err(host(dv), rdv))
+            report(name, **e)
+            assert dk.shape == (1, hkv, n, d) and dv.shape == (1, hkv, n, d)
+            assert e["o"] <= TOL_BF16 and e["lse"] <= TOL_LSE and e["dq"] <= TOL_BF16, (name, e)
+            assert e["dk"] <= TOL_BF16 * math.sqrt(g) and e["dv"] <= TOL_BF16 * math.sqrt(g), (name, e)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_blocksparse_grouped_query_equals_repeated_kv(d):
+    for causal in (False, True):
+        for H, hkv, N in ((8, 2, 1000), (4, 1, 333)):
+            announce(f"sparse gqa == repeated K/V H={H} H_kv={hkv} N={N} d={d} causal={causal}")
+            nb = -(-N // 128)
+            mask = inputs.random_block_mask(34 + N, nb, 0.4, causal)
+            _repeat_equivalence(2, H, hkv, N, d, causal, 35 + N + d, mask)
+
+
 def test_autograd_wrapper_grouped_query():
     """api.attention with 8 query heads on 2 K/V heads: output and gradients (dK, dV of the
     shared heads' shape) equal the explicit fa_fwd_gqa / fa_bwd_gqa calls bit for bit."""
@@ -142,6 +188,27 @@ def test_autograd_wrapper_grouped_query():
     out.backward(dev(do, BF))
     o, lse = api.forward(tq.detach(), tk.detach(), tv.detach(), None, True)
     eq = api.backward(tq.detach(), tk.detach(), tv.detach(), o, lse, dev(do, BF), None, True, grad_dtype=BF)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), o)
+    assert tk.grad.shape == tk.shape and tv.grad.shape == tv.shape
+    for g, e in zip((tq.grad, tk.grad, tv.grad), eq):
+        assert torch.equal(g, e)
+
+
+def test_autograd_wrapper_grouped_query_with_block_mask():
+    """api.attention with 8 query heads on 2 K/V heads and a block mask: output and gradients
+    equal the explicit fa_fwd_blocksparse_gqa / fa_bwd_blocksparse_gqa calls bit for bit."""
+    announce("autograd wrapper, grouped-query, block-sparse")
+    n = 400
+    q, k, v, do = inputs.random_case(36, 1, 8, n, 64, "bf16", backward=True, h_kv=2)
+    mask = inputs.random_block_mask(37, -(-n // 128), 0.5, True)
+    tm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda:0")
+    tq, tk, tv = (dev(x, BF).requires_grad_(True) for x in (q, k, v))
+    out = api.attention(tq, tk, tv, None, True, tm)
+    out.backward(dev(do, BF))
+    o, lse = api.forward_blocksparse(tq.detach(), tk.detach(), tv.detach(), tm, None, True)
+    eq = api.backward(tq.detach(), tk.detach(), tv.detach(), o, lse, dev(do, BF), None, True, grad_dtype=BF,
+                      block_mask=tm)
     torch.cuda.synchronize()
     assert torch.equal(out.detach(), o)
     assert tk.grad.shape == tk.shape and tv.grad.shape == tv.shape
