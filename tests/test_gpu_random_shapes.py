@@ -1,0 +1,79 @@
+"""Seeded mixed-configuration parity sweep.
+
+Sixteen configurations drawn once from a fixed seed: batch, heads, shared K/V heads
+(grouped-/multi-query), ragged length N, head dimension, causal or not, a random
+block mask or none, and fp32 or bf16 gradient outputs.  For each one the forward
+(O, lse) and the backward (dQ, dK, dV) are compared element by element with the
+fp64 oracle.  Gates as in the dedicated tests: bf16 outputs within 2e-2, lse within
+1e-3; dK/dV of a shared head are sums over its g query heads, so their gate grows
+by sqrt(g); bf16 gradient outputs add one rounding of up to 2^-8 of each value,
+hence twice the gate.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from exact_attention_35_amd import api, inputs
+from gpu_util import TOL_BF16, TOL_LSE, announce, dev, host, max_err, report
+
+pytestmark = pytest.mark.gpu
+
+BF = torch.bfloat16
+
+
+def _draw_cases(count=16):
+    rng = np.random.default_rng(np.random.SeedSequence([2718, 281]))
+    cases = []
+    for i in range(count):
+        B = int(rng.integers(1, 3))
+        H = int(rng.choice([1, 2, 3, 4, 6, 8]))
+        divisors = [g for g in range(1, H + 1) if H % g == 0]
+        hkv = int(rng.choice(divisors))
+        N = int(rng.integers(1, 701))
+        d = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        density = float(rng.choice([0.0, 0.3, 0.7])) if rng.random() < 0.4 else None
+        grad_bf16 = bool(rng.random() < 0.3)
+        cases.append((i, B, H, hkv, N, d, causal, density, grad_bf16))
+    return cases
+
+
+CASES = _draw_cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"case{c[0]}" for c in CASES])
+def test_random_configuration(case):
+    i, B, H, hkv, N, d, causal, density, grad_bf16 = case
+    name = (f"random case {i}: B={B} H={H} H_kv={hkv} N={N} d={d} causal={causal} "
+            f"mask={'none' if density is None else density} grads={'bf16' if grad_bf16 else 'fp32'}")
+    announce(name)
+    q, k, v, do = inputs.random_case(400 + i, B, H, N, d, "bf16", backward=True, h_kv=hkv)
+    scale = api.default_scale(d)
+    mask = None
+    tm = None
+    if density is not None:
+        nb = -(-N // inputs.MASK_BLOCK)
+        mask = inputs.random_block_mask(500 + i, nb, density, causal)
+        tm = torch.from_numpy(np.ascontiguousarray(mask)).to("cuda:0")
+    tq, tk, tv, tdo = dev(q, BF), dev(k, BF), dev(v, BF), dev(do, BF)
+    if tm is None:
+        o, lse = api.forward(tq, tk, tv, scale, causal)
+    else:
+        o, lse = api.forward_blocksparse(tq, tk, tv, tm, scale, causal)
+    dq, dk, dv = api.backward(tq, tk, tv, o, lse, tdo, scale, causal, grad_dtype=BF if grad_bf16 else torch.float32,
+                              block_mask=tm)
+    torch.cuda.synchronize()
+    ro, rl = oracle.forward(q, k, v, scale, causal, mask, inputs.MASK_BLOCK)
+    rq, rk, rv = oracle.backward(q, k, v, do, scale, causal, mask, inputs.MASK_BLOCK)
+    e = dict(o=max_err(host(o), ro), lse=max_err(host(lse), rl), dq=max_err(host(dq), rq),
+             dk=max_err(host(dk), rk), dv=max_err(host(dv), rv))
+    report(name, **e)
+    assert dk.shape == (B, hkv, N, d) and dv.shape == (B, hkv, N, d)
+    gate = TOL_BF16 * (2.0 if grad_bf16 else 1.0)
+    assert e["o"] <= TOL_BF16 and e["lse"] <= TOL_LSE, (name, e)
+    assert e["dq"] <= gate, (name, e)
+    assert max(e["dk"], e["dv"]) <= gate * math.sqrt(H // hkv), (name, e)
