@@ -396,7 +396,9 @@ __device__ __forceinline__ float exp_tile8(const f32x16 (&s)[BN / 32], const flo
       const float p2 = __builtin_amdgcn_exp2f(fmaf(s[b][r + 2], ct, -mc));
       const float p3 = __builtin_amdgcn_exp2f(fmaf(s[b][r + 3], ct, -mc));
       lsum += (p0 + p1) + (p2 + p3);
-      pf[g][w] = cvt_fp8x2<true>(p2, p3, cvt_fp8x2<false>(p0, p1, 0));
+      // both halves are overwritten: passing the previous tile's (consumed) fragment as
+      // the preserved input lets the conversion write in place, without zeroing first
+      pf[g][w] = cvt_fp8x2<true>(p2, p3, cvt_fp8x2<false>(p0, p1, pf[g][w]));
     }
   }
   return lsum;
