@@ -316,7 +316,7 @@ MEASURED_TRAFFIC = {
     # bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel
     "bwd": {"fetch_kib": 66575.2 + 366495.1 + 317539.1, "write_kib": 2048.0 + 262144.0 + 131072.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "49bca1beb47670b8024c6e33900769b6751ca78413544b5ffd2742a4a66d5aca"},
+            "sha256": "43fdbd0364bbf1460cbe576257b8918842c6376359c4244a3b66c0b889673f7f"},
 }
 
 

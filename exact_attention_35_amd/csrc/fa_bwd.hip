@@ -821,6 +821,7 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdF32Args a) {
   constexpr int BK = 16;
   __shared__ float kk[BK * D];
   __shared__ float vv[BK * D];
+  __shared__ float dos[BQ * (D + 1)];  // each thread's dO row (stride D + 1: no bank conflicts)
   const int tid = threadIdx.x;
   const int N = a.N;
   const int qt = (int)(blockIdx.x / a.BH);
@@ -829,7 +830,8 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdF32Args a) {
   const size_t kvoff = (size_t)(bh / a.group) * N * D;
   const int qi = qt * BQ + tid;
   const bool in = qi < N;
-  float qv[D], dov[D], g[D];
+  float qv[D], g[D];
+  float* const dov = dos + tid * (D + 1);
 #pragma unroll
   for (int t = 0; t < D; ++t) {
     qv[t] = in ? a.q[hoff + (size_t)qi * D + t] : 0.f;
@@ -859,6 +861,9 @@ __global__ __launch_bounds__(64) void bwd_f32_dq_kernel(BwdF32Args a) {
         }
         const float p = expf(sd * a.scale - l);
         const float ds = p * (dpd - dl);
+        // read the key row from LDS again rather than keep it in D registers since the dot
+        // product (at d = 128 that would spill)
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int t = 0; t < D; ++t) g[t] = fmaf(ds, kk[j * D + t], g[t]);
       }
