@@ -314,9 +314,9 @@ MEASURED_TRAFFIC = {
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
             "sha256": "ce10357b2478a6bf8739845889e411e5778bc26311878750502524b3f0881268"},
     # bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel
-    "bwd": {"fetch_kib": 66575.2 + 366495.1 + 317539.1, "write_kib": 2048.0 + 262144.0 + 131072.0,
+    "bwd": {"fetch_kib": 66575.4 + 366484.7 + 319621.4, "write_kib": 2048.0 + 262144.0 + 131072.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "43fdbd0364bbf1460cbe576257b8918842c6376359c4244a3b66c0b889673f7f"},
+            "sha256": "5694f7125a291010990f447f0e80002591ffc4ddb6dafb8c98d561bb37774d48"},
 }
 
 

@@ -378,7 +378,11 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
       if (active) dma_k<D, BN, NW>(kres, knext, tile_at(t + 1), wi, lane);
       if (t >= 1 && t - 1 < ntiles) vector_phase(t - 1);
     }
-    barrier_plain();
+    // The mid-step barrier only keeps the two groups' phases in alternation: the ring
+    // buffers need just the end-of-step barrier (every buffer written in step t was last
+    // read in step t - 1).  Dense, the groups run faster left to drift; block-sparse,
+    // where the two tile streams differ in length, the barrier keeps them in step.
+    if (SPARSE) barrier_plain();
     if (grp == 0) {
       if (t < ntiles) vector_phase(t);
       wait_lgkm_vm<LPW>();  // V(t+1) has landed
