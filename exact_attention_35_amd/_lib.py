@@ -20,11 +20,11 @@ FA_F32 = 0
 FA_BF16 = 1
 FA_MASK_BLOCK = 128
 FA_FP8_BLOCK = 128
-FA_ABI_VERSION = 4  # must equal FA_ABI_VERSION of include/fa.h
+FA_ABI_VERSION = 5  # must equal FA_ABI_VERSION of include/fa.h
 
 EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_blocksparse", "fa_bwd_workspace_size", "fa_bwd",
            "fa_bwd_gqa_workspace_size", "fa_bwd_gqa", "fa_bwd_blocksparse", "fa_fwd_blocksparse_gqa",
-           "fa_bwd_blocksparse_gqa", "fa_quantize_fp8", "fa_fwd_fp8",
+           "fa_bwd_blocksparse_gqa", "fa_fwd_ex", "fa_bwd_ex", "fa_quantize_fp8", "fa_fwd_fp8",
            "fa_status_string", "fa_version")
 
 _lib = None
@@ -85,6 +85,10 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_blocksparse_gqa.restype = _i
     lib.fa_bwd_blocksparse_gqa.argtypes = [_vp] * 10 + [_i, _i, _i, _i, _i, _f, _i, _i, _i, _vp, ctypes.c_size_t,
                                                         _vp]
+    lib.fa_fwd_ex.restype = _i
+    lib.fa_fwd_ex.argtypes = [_vp] * 7 + [_i] * 5 + [_f, _i, _i, _vp]
+    lib.fa_bwd_ex.restype = _i
+    lib.fa_bwd_ex.argtypes = [_vp] * 11 + [_i] * 5 + [_f, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
     _lib = lib
     return lib
 

@@ -41,6 +41,37 @@ def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, allow_gqa: boo
     return q.shape
 
 
+def _check_buffer(t: torch.Tensor, shape, dtype: torch.dtype, device: torch.device, name: str) -> None:
+    """A caller-supplied buffer must be exactly what the kernels will address: they write or
+    read every element of `shape` in `dtype`, so anything else would be accessed out of bounds."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}; "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def _outputs(q: torch.Tensor, out, lse_out, with_lse: bool):
+    """o (caller's `out` or new) and lse (caller's `lse_out`, new, or None), checked."""
+    B, H, N, _ = q.shape
+    if out is None:
+        o = torch.empty_like(q)
+    else:
+        _check_buffer(out, q.shape, q.dtype, q.device, "out")
+        o = out
+    lse = None
+    if with_lse:
+        if lse_out is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        else:
+            _check_buffer(lse_out, (B, H, N), torch.float32, q.device, "lse_out")
+            lse = lse_out
+    elif lse_out is not None:
+        raise ValueError("lse_out given with with_lse=False")
+    return o, lse
+
+
 def default_scale(d: int) -> float:
     """1/sqrt(d) as the fp32 value the kernels receive."""
     return float(torch.tensor(1.0, dtype=torch.float32) / torch.tensor(float(d), dtype=torch.float32).sqrt())
@@ -57,10 +88,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[f
     B, H, N, d = _check_qkv(q, k, v, allow_gqa=True)
     hkv = k.shape[1]
     scale = default_scale(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
-    lse = None
-    if with_lse:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    o, lse = _outputs(q, out, lse_out, with_lse)
     lib = _lib.load()
     lse_ptr = lse.data_ptr() if lse is not None else None
     with torch.cuda.device(q.device):
@@ -86,10 +114,7 @@ def forward_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
     hkv = k.shape[1]
     _check_mask(block_mask, N, q.device)
     scale = default_scale(d) if scale is None else float(scale)
-    o = torch.empty_like(q) if out is None else out
-    lse = None
-    if with_lse:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse_out is None else lse_out
+    o, lse = _outputs(q, out, lse_out, with_lse)
     lib = _lib.load()
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), block_mask.data_ptr(), o.data_ptr(),
             lse.data_ptr() if lse is not None else None)
@@ -101,6 +126,42 @@ def forward_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
             st = lib.fa_fwd_blocksparse_gqa(*ptrs, B, H, hkv, *tail)
     _lib.check(st, "fa_fwd_blocksparse" if hkv == H else "fa_fwd_blocksparse_gqa")
     return o, lse
+
+
+def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+                  causal: bool = False, block_mask: Optional[torch.Tensor] = None,
+                  out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+                  o_lo_out: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, torch.Tensor, Optional[torch.Tensor]]:
+    """Forward for training (fa_fwd_ex): (o, lse, o_lo).
+
+    For bf16 inputs o_lo is the low-order bf16 part of the output (o + o_lo carries the fp32
+    result); hand it to backward(..., o_lo=o_lo) so that D = rowsum(dO * O) is formed from it.
+    For fp32 inputs o_lo is None.  block_mask and grouped-query K/V as for forward_blocksparse.
+    """
+    B, H, N, d = _check_qkv(q, k, v, allow_gqa=True)
+    hkv = k.shape[1]
+    if block_mask is not None:
+        _check_mask(block_mask, N, q.device)
+    scale = default_scale(d) if scale is None else float(scale)
+    o, lse = _outputs(q, out, lse_out, True)
+    o_lo = None
+    if q.dtype == torch.bfloat16:
+        if o_lo_out is None:
+            o_lo = torch.empty_like(q)
+        else:
+            _check_buffer(o_lo_out, q.shape, q.dtype, q.device, "o_lo_out")
+            o_lo = o_lo_out
+    elif o_lo_out is not None:
+        raise ValueError("o_lo_out applies to bfloat16 inputs only")
+    lib = _lib.load()
+    with torch.cuda.device(q.device):
+        st = lib.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           None if block_mask is None else block_mask.data_ptr(), o.data_ptr(),
+                           None if o_lo is None else o_lo.data_ptr(), lse.data_ptr(), B, H, hkv, N, d, scale,
+                           int(bool(causal)), _DTYPES[q.dtype], _stream_ptr(q.device))
+    _lib.check(st, "fa_fwd_ex")
+    return o, lse, o_lo
 
 
 def bwd_workspace_size(B: int, H: int, N: int, d: int, grad_dtype: torch.dtype = torch.float32,
@@ -121,13 +182,16 @@ def _check_mask(block_mask: torch.Tensor, N: int, device: torch.device) -> None:
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
              do: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
              grad_dtype: torch.dtype = torch.float32, workspace: Optional[torch.Tensor] = None,
-             block_mask: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+             block_mask: Optional[torch.Tensor] = None, o_lo: Optional[torch.Tensor] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Gradients (dq, dk, dv) of sum(do * o), in grad_dtype (float32 by default).
 
     With block_mask (uint8 [ceil(N/128), ceil(N/128)], as for forward_blocksparse) this is
     the block-sparse backward, fa_bwd_blocksparse.  With k and v of H_kv < H heads it is the
     grouped-query backward, fa_bwd_gqa (with a mask too: fa_bwd_blocksparse_gqa); dk and dv
-    then have k's shape.
+    then have k's shape.  With o_lo (from forward_train) the call is fa_bwd_ex, which forms
+    D = rowsum(do * O) from o + o_lo.  `workspace`, if given, is a contiguous uint8 tensor on
+    q's device of at least bwd_workspace_size(...) bytes.
     """
     B, H, N, d = _check_qkv(q, k, v, allow_gqa=True)
     hkv = k.shape[1]
@@ -138,6 +202,10 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             raise ValueError(f"{name} must match q in shape, dtype and device, and be contiguous")
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be contiguous float32 [B, H, N] on q's device")
+    if o_lo is not None:
+        if q.dtype != torch.bfloat16:
+            raise ValueError("o_lo applies to bfloat16 inputs only")
+        _check_buffer(o_lo, q.shape, q.dtype, q.device, "o_lo")
     if grad_dtype not in _DTYPES:
         raise ValueError("grad_dtype must be torch.float32 or torch.bfloat16")
     scale = default_scale(d) if scale is None else float(scale)
@@ -147,13 +215,20 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     need = bwd_workspace_size(B, H, N, d, grad_dtype, hkv)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif (not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or workspace.dim() != 1
+          or not workspace.is_contiguous() or workspace.device != q.device or workspace.numel() < need):
+        raise ValueError(f"workspace must be a contiguous 1-d uint8 tensor of at least {need} bytes on {q.device}")
     lib = _lib.load()
     tail = (N, d, scale, int(bool(causal)), _DTYPES[q.dtype], _DTYPES[grad_dtype], workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
     with torch.cuda.device(q.device):
-        if block_mask is not None and hkv == H:
+        if o_lo is not None:
+            name = "fa_bwd_ex"
+            st = lib.fa_bwd_ex(*ptrs[:3], None if block_mask is None else block_mask.data_ptr(), ptrs[3],
+                               o_lo.data_ptr(), *ptrs[4:], B, H, hkv, *tail)
+        elif block_mask is not None and hkv == H:
             name = "fa_bwd_blocksparse"
             st = lib.fa_bwd_blocksparse(*ptrs[:3], block_mask.data_ptr(), *ptrs[3:], B, H, *tail)
         elif block_mask is not None:
@@ -170,26 +245,23 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
 
 
 class FlashAttentionFunction(torch.autograd.Function):
-    """autograd wrapper: forward saves (q, k, v, o, lse[, block_mask]); backward calls fa_bwd
-    (fa_bwd_gqa, fa_bwd_blocksparse, fa_bwd_blocksparse_gqa)."""
+    """autograd wrapper: forward (fa_fwd_ex) saves q, k, v, o, lse, the low-order part of o
+    (bf16 inputs) and the block mask; backward calls fa_bwd_ex with them (fp32 inputs: fa_bwd
+    and its variants)."""
 
     @staticmethod
     def forward(ctx, q, k, v, scale=None, causal=False, block_mask=None):
-        if block_mask is None:
-            o, lse = forward(q, k, v, scale, causal)
-            ctx.save_for_backward(q, k, v, o, lse)
-        else:
-            o, lse = forward_blocksparse(q, k, v, block_mask, scale, causal)
-            ctx.save_for_backward(q, k, v, o, lse, block_mask)
+        o, lse, o_lo = forward_train(q, k, v, scale, causal, block_mask)
+        ctx.save_for_backward(q, k, v, o, lse, o_lo, block_mask)
         ctx.scale = default_scale(q.shape[-1]) if scale is None else float(scale)
         ctx.causal = causal
         return o
 
     @staticmethod
     def backward(ctx, do):
-        q, k, v, o, lse, *mask = ctx.saved_tensors
+        q, k, v, o, lse, o_lo, mask = ctx.saved_tensors
         dq, dk, dv = backward(q, k, v, o, lse, do.contiguous(), ctx.scale, ctx.causal, grad_dtype=q.dtype,
-                              block_mask=mask[0] if mask else None)
+                              block_mask=mask, o_lo=o_lo)
         return dq, dk, dv, None, None, None
 
 

@@ -50,25 +50,30 @@ size_t elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
 // grouped-query: H_kv K/V heads, each shared by H / H_kv consecutive query heads
 bool valid_kv_heads(int H, int Hkv) { return Hkv >= 1 && Hkv <= H && H % Hkv == 0; }
 
-int fwd_impl(const void* q, const void* k, const void* v, const unsigned char* mask, void* o, float* lse,
-             int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype, void* stream, bool sparse) {
+int fwd_impl(const void* q, const void* k, const void* v, const unsigned char* mask, void* o, void* o_lo,
+             float* lse, int B, int H, int Hkv, int N, int d, float scale, int causal, int dtype, void* stream,
+             bool sparse) {
   int st = check_common(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (!valid_kv_heads(H, Hkv)) return FA_ERR_INVALID_ARG;
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (sparse && !mask) return FA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+  if (o_lo && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)) ||
+      (o_lo && !aligned16(o_lo)))
     return FA_ERR_INVALID_ARG;
   const size_t n = (size_t)B * H * N;
   const size_t tb = n * d * elem_bytes(dtype);
   const size_t kvb = (size_t)B * Hkv * N * d * elem_bytes(dtype);
   const Range in[3] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb)};
-  const Range ro = range_of(o, tb);
-  for (const Range& r : in) {
-    if (overlap(ro, r)) return FA_ERR_INVALID_ARG;
-    if (lse && overlap(range_of(lse, n * 4), r)) return FA_ERR_INVALID_ARG;
+  // outputs: o, then the optional lse and o_lo (an empty range when absent)
+  const Range outs[3] = {range_of(o, tb), range_of(lse, lse ? n * 4 : 0), range_of(o_lo, o_lo ? tb : 0)};
+  for (int i = 0; i < 3; ++i) {
+    for (const Range& r : in)
+      if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return FA_ERR_INVALID_ARG;
   }
-  if (lse && overlap(range_of(lse, n * 4), ro)) return FA_ERR_INVALID_ARG;
   if (sparse) {
     if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
     const size_t nb = ((size_t)N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
@@ -76,13 +81,15 @@ int fwd_impl(const void* q, const void* k, const void* v, const unsigned char* m
     const size_t list_bytes = (2 * nb * 2 + 15) & ~(size_t)15;
     if (kFwdStaticLds + list_bytes > kLdsBytes) return FA_ERR_UNSUPPORTED;
     const Range rm = range_of(mask, nb * nb);
-    if (overlap(rm, ro) || (lse && overlap(rm, range_of(lse, n * 4)))) return FA_ERR_INVALID_ARG;
+    for (const Range& r : outs)
+      if (overlap(rm, r)) return FA_ERR_INVALID_ARG;
   }
   fa::FwdParams p;
   p.q = q;
   p.k = k;
   p.v = v;
   p.o = o;
+  p.o_lo = o_lo;
   p.lse = lse;
   p.mask = sparse ? mask : nullptr;
   p.B = B;
@@ -124,23 +131,29 @@ const char* fa_status_string(int status) {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
            float scale, int causal, int dtype, void* stream) {
-  return fwd_impl(q, k, v, nullptr, o, lse, B, H, H, N, d, scale, causal, dtype, stream, false);
+  return fwd_impl(q, k, v, nullptr, o, nullptr, lse, B, H, H, N, d, scale, causal, dtype, stream, false);
 }
 
 int fa_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int H_kv, int N,
                int d, float scale, int causal, int dtype, void* stream) {
-  return fwd_impl(q, k, v, nullptr, o, lse, B, H, H_kv, N, d, scale, causal, dtype, stream, false);
+  return fwd_impl(q, k, v, nullptr, o, nullptr, lse, B, H, H_kv, N, d, scale, causal, dtype, stream, false);
 }
 
 int fa_fwd_blocksparse(const void* q, const void* k, const void* v, const unsigned char* block_mask, void* o,
                        float* lse, int B, int H, int N, int d, float scale, int causal, int dtype, void* stream) {
-  return fwd_impl(q, k, v, block_mask, o, lse, B, H, H, N, d, scale, causal, dtype, stream, true);
+  return fwd_impl(q, k, v, block_mask, o, nullptr, lse, B, H, H, N, d, scale, causal, dtype, stream, true);
 }
 
 int fa_fwd_blocksparse_gqa(const void* q, const void* k, const void* v, const unsigned char* block_mask, void* o,
                            float* lse, int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype,
                            void* stream) {
-  return fwd_impl(q, k, v, block_mask, o, lse, B, H, H_kv, N, d, scale, causal, dtype, stream, true);
+  return fwd_impl(q, k, v, block_mask, o, nullptr, lse, B, H, H_kv, N, d, scale, causal, dtype, stream, true);
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, const unsigned char* block_mask, void* o, void* o_lo,
+              float* lse, int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype, void* stream) {
+  return fwd_impl(q, k, v, block_mask, o, o_lo, lse, B, H, H_kv, N, d, scale, causal, dtype, stream,
+                  block_mask != nullptr);
 }
 
 size_t fa_bwd_gqa_workspace_size(int B, int H, int H_kv, int N, int d, int grad_dtype) {
@@ -163,16 +176,17 @@ namespace {
 constexpr size_t bwd_dkdv_static_lds(int d) { return d == 128 ? 132608 + 64 : 83456 + 64; }
 constexpr size_t kBwdDqStaticLds = (size_t)6 * 16384 + 256;
 
-int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* mask, const void* o, const float* lse,
-             const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale,
-             int causal, int dtype, int grad_dtype, void* workspace, size_t workspace_bytes, void* stream,
-             bool sparse) {
+int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* mask, const void* o, const void* o_lo,
+             const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+             float scale, int causal, int dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
+             void* stream, bool sparse) {
   int st = check_common(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (!valid_kv_heads(H, Hkv)) return FA_ERR_INVALID_ARG;
   if (grad_dtype != FA_F32 && grad_dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (dtype == FA_F32 && grad_dtype != FA_F32) return FA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  if (o_lo && (dtype != FA_BF16 || !aligned16(o_lo))) return FA_ERR_INVALID_ARG;
   const void* ptrs[] = {q, k, v, o, lse, dO, dq, dk, dv};
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_INVALID_ARG;
@@ -193,8 +207,9 @@ int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* m
   const size_t kvb = nkv * d * elem_bytes(dtype);
   const size_t gb = n * d * elem_bytes(grad_dtype);
   const size_t gkvb = nkv * d * elem_bytes(grad_dtype);
-  const Range ins[6] = {range_of(q, tb), range_of(k, kvb), range_of(v, kvb),
-                        range_of(o, tb), range_of(lse, n * 4), range_of(dO, tb)};
+  const Range ins[7] = {range_of(q, tb),      range_of(k, kvb), range_of(v, kvb),
+                        range_of(o, tb),      range_of(lse, n * 4), range_of(dO, tb),
+                        range_of(o_lo, o_lo ? tb : 0)};
   const Range outs[4] = {range_of(dq, gb), range_of(dk, gkvb), range_of(dv, gkvb), range_of(workspace, need)};
   for (int i = 0; i < 4; ++i) {
     for (const Range& r : ins)
@@ -211,6 +226,7 @@ int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* m
   p.k = k;
   p.v = v;
   p.o = o;
+  p.o_lo = o_lo;
   p.lse = lse;
   p.dO = dO;
   p.dq = dq;
@@ -245,31 +261,39 @@ extern "C" {
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
            void* dk, void* dv, int B, int H, int N, int d, float scale, int causal, int dtype, int grad_dtype,
            void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(q, k, v, nullptr, o, lse, dO, dq, dk, dv, B, H, H, N, d, scale, causal, dtype, grad_dtype,
-                  workspace, workspace_bytes, stream, false);
+  return bwd_impl(q, k, v, nullptr, o, nullptr, lse, dO, dq, dk, dv, B, H, H, N, d, scale, causal,
+                  dtype, grad_dtype, workspace, workspace_bytes, stream, false);
 }
 
 int fa_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
                void* dk, void* dv, int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype,
                int grad_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(q, k, v, nullptr, o, lse, dO, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype, grad_dtype,
-                  workspace, workspace_bytes, stream, false);
+  return bwd_impl(q, k, v, nullptr, o, nullptr, lse, dO, dq, dk, dv, B, H, H_kv, N, d, scale, causal,
+                  dtype, grad_dtype, workspace, workspace_bytes, stream, false);
 }
 
 int fa_bwd_blocksparse(const void* q, const void* k, const void* v, const unsigned char* block_mask, const void* o,
                        const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                        float scale, int causal, int dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  return bwd_impl(q, k, v, block_mask, o, lse, dO, dq, dk, dv, B, H, H, N, d, scale, causal, dtype, grad_dtype,
-                  workspace, workspace_bytes, stream, true);
+  return bwd_impl(q, k, v, block_mask, o, nullptr, lse, dO, dq, dk, dv, B, H, H, N, d, scale, causal,
+                  dtype, grad_dtype, workspace, workspace_bytes, stream, true);
 }
 
 int fa_bwd_blocksparse_gqa(const void* q, const void* k, const void* v, const unsigned char* block_mask,
                            const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, int B,
                            int H, int H_kv, int N, int d, float scale, int causal, int dtype, int grad_dtype,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(q, k, v, block_mask, o, lse, dO, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype, grad_dtype,
-                  workspace, workspace_bytes, stream, true);
+  return bwd_impl(q, k, v, block_mask, o, nullptr, lse, dO, dq, dk, dv, B, H, H_kv, N, d, scale, causal,
+                  dtype, grad_dtype, workspace, workspace_bytes, stream, true);
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const unsigned char* block_mask, const void* o,
+              const void* o_lo, const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+              int H_kv, int N, int d, float scale, int causal, int dtype, int grad_dtype, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, block_mask, o, o_lo, lse, dO, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype,
+                  grad_dtype, workspace, workspace_bytes, stream, block_mask != nullptr);
 }
 
 }  // extern "C"

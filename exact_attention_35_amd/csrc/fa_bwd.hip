@@ -34,11 +34,12 @@ namespace fa {
 
 // ---------------------------------------------------------------------------
 // stats[row] = (lse * log2 e, -D) with D = rowsum(dO * O).  T = unsigned short (bf16 bits) or float.
+// With olo (bf16 only), O is taken as o + olo, the stored output plus its low-order part.
 // ---------------------------------------------------------------------------
 template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, const T* __restrict__ dO,
-                                                       const float* __restrict__ lse, float2* __restrict__ stats,
-                                                       long long rows) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, const T* __restrict__ olo,
+                                                       const T* __restrict__ dO, const float* __restrict__ lse,
+                                                       float2* __restrict__ stats, long long rows) {
   constexpr int EPT = 16 / sizeof(T);  // elements per 16-byte load
   constexpr int TPR = D / EPT;         // threads per row
   constexpr int RPB = 256 / TPR;       // rows per block
@@ -52,8 +53,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, 
     if (sizeof(T) == 2) {
       const unsigned short* a = reinterpret_cast<const unsigned short*>(&ov);
       const unsigned short* b = reinterpret_cast<const unsigned short*>(&dv);
+      if (olo != nullptr) {
+        const uint4 lv = *reinterpret_cast<const uint4*>(olo + row * D + part * EPT);
+        const unsigned short* c = reinterpret_cast<const unsigned short*>(&lv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf(bf16_bits_to_float(a[e]), bf16_bits_to_float(b[e]), acc);
+        for (int e = 0; e < 8; ++e) {
+          const float g = bf16_bits_to_float(b[e]);
+          acc = fmaf(bf16_bits_to_float(a[e]), g, fmaf(bf16_bits_to_float(c[e]), g, acc));
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(bf16_bits_to_float(a[e]), bf16_bits_to_float(b[e]), acc);
+      }
     } else {
       const float* a = reinterpret_cast<const float*>(&ov);
       const float* b = reinterpret_cast<const float*>(&dv);
@@ -937,7 +948,8 @@ static void launch_prep(const BwdParams& p, hipStream_t stream) {
   const long long rows = (long long)p.B * p.H * p.N;
   const unsigned blocks = (unsigned)((rows + RPB - 1) / RPB);
   hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, static_cast<const T*>(p.o),
-                     static_cast<const T*>(p.dO), p.lse, reinterpret_cast<float2*>(p.stats), rows);
+                     static_cast<const T*>(p.o_lo), static_cast<const T*>(p.dO), p.lse,
+                     reinterpret_cast<float2*>(p.stats), rows);
 }
 
 template <int D, bool CAUSAL, bool SPARSE>

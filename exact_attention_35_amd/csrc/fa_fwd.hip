@@ -38,6 +38,7 @@ struct FwdKernelArgs {
   const unsigned short* k;
   const unsigned short* v;
   unsigned short* o;
+  unsigned short* olo;  // optional low-order part of O (null: not written)
   float* lse;
   const unsigned char* mask;
   int BH;
@@ -386,20 +387,32 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   }
   wait_dma();  // no LDS-direct load may outlive the workgroup
 
-  // ---- epilogue
+  // ---- epilogue: O = acc / l in bf16; optionally its low-order part, bf16(O - fp32(bf16(O))),
+  // so that the two together carry O to about 16 significant bits
   const float l = xhalf_sum(l_half);
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  const bool want_lo = a.olo != nullptr;
+  const BufRes lores = make_buf(want_lo ? a.olo + hoff : a.o + hoff, head_bytes);
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int d0 = 32 * db + 8 * i + 4 * half;
-      uint2 pk;
-      pk.x = (unsigned int)float_to_bf16_bits(oacc[db][4 * i + 0] * inv) |
-             ((unsigned int)float_to_bf16_bits(oacc[db][4 * i + 1] * inv) << 16);
-      pk.y = (unsigned int)float_to_bf16_bits(oacc[db][4 * i + 2] * inv) |
-             ((unsigned int)float_to_bf16_bits(oacc[db][4 * i + 3] * inv) << 16);
+      unsigned short hb[4], lb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = oacc[db][4 * i + e] * inv;
+        hb[e] = float_to_bf16_bits(x);
+        lb[e] = float_to_bf16_bits(x - bf16_bits_to_float(hb[e]));  // exact difference, then rounded
+      }
+      const uint2 pk = make_uint2((unsigned int)hb[0] | ((unsigned int)hb[1] << 16),
+                                  (unsigned int)hb[2] | ((unsigned int)hb[3] << 16));
       buf_store8(ores, (unsigned int)(qrow * D + d0) * 2, pk);  // rows past N are dropped
+      if (want_lo) {
+        const uint2 pl = make_uint2((unsigned int)lb[0] | ((unsigned int)lb[1] << 16),
+                                    (unsigned int)lb[2] | ((unsigned int)lb[3] << 16));
+        buf_store8(lores, (unsigned int)(qrow * D + d0) * 2, pl);
+      }
     }
   }
   if (a.lse != nullptr && half == 0 && qrow < N) {
@@ -506,6 +519,7 @@ static hipError_t launch_fwd_bf16_t(const FwdParams& p, hipStream_t stream) {
   a.k = static_cast<const unsigned short*>(p.k);
   a.v = static_cast<const unsigned short*>(p.v);
   a.o = static_cast<unsigned short*>(p.o);
+  a.olo = static_cast<unsigned short*>(p.o_lo);
   a.lse = p.lse;
   a.mask = p.mask;
   a.BH = p.B * p.H;

@@ -12,6 +12,7 @@ struct FwdParams {
   const void* k;
   const void* v;
   void* o;
+  void* o_lo;                 // bf16 only: low-order part of O, bf16(O - bf16(O)); may be null
   float* lse;                 // may be null
   const unsigned char* mask;  // block-sparse tile mask, null when dense
   int B, H, N, d;
@@ -26,6 +27,7 @@ struct BwdParams {
   const void* k;
   const void* v;
   const void* o;
+  const void* o_lo;  // bf16 only: low-order part of O (D is then formed from o + o_lo); may be null
   const float* lse;
   const void* dO;
   void* dq;

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 #define FA_MASK_BLOCK 128 /* rows and keys covered by one block-sparse mask entry */
 #define FA_FP8_BLOCK 128  /* rows of one head that share one fp8 scale */
 
@@ -70,6 +70,10 @@ enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 };
  * Forward.  o <- attention(q, k, v) as defined above; lse <- the row
  * log-sum-exp (may be NULL when the caller does not need it, e.g. inference).
  * scale is any finite float (typically 1/sqrt(d)); causal is 0 or 1.
+ * Extents: q, o hold B*H*N*d elements and so do k and v -- this call reads
+ * B*H*N*d elements of each of k and v (one K/V head per query head).  K/V with
+ * fewer heads must go to fa_fwd_gqa, which reads B*H_kv*N*d of each; handing
+ * such buffers to fa_fwd reads past their end.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int causal, int dtype, void* stream);
@@ -113,6 +117,8 @@ size_t fa_bwd_workspace_size(int B, int H, int N, int d, int grad_dtype);
  * requires dtype FA_BF16).  The workspace must hold fa_bwd_workspace_size()
  * bytes; its contents on entry do not matter.  Every gradient element is
  * reduced by one thread in a fixed order: results are deterministic.
+ * Extents: as fa_fwd, this call reads B*H*N*d elements of each of k and v and
+ * writes B*H*N*d of each of dk and dv; grouped-query K/V go to fa_bwd_gqa.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
            void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int causal,
@@ -214,6 +220,38 @@ int fa_quantize_fp8(const void* x, const signed char* signs, unsigned char* code
  * / sum P per element.  O is rounded to bf16.
  * Arguments and errors as fa_fwd_gqa.
  */
+/*
+ * General forward: every variant above in one call, plus an optional second
+ * output for training.  block_mask: NULL (dense) or a mask as for
+ * fa_fwd_blocksparse; k, v: [B, H_kv, N, d] as for fa_fwd_gqa (H_kv == H: one
+ * K/V head per query head).  o_lo: NULL, or (bf16 only) a [B, H, N, d] bf16
+ * buffer that receives the low-order part of the output, o_lo = bf16(O - o)
+ * where O is the fp32 result before its rounding to o; o + o_lo then carries O
+ * to about 16 significant bits (relative error <= 2^-17).  Passing it on to
+ * fa_bwd_ex lets the backward form D = rowsum(dO * O) from that O instead of
+ * from the bf16 o (D's rounding error then no longer dominates the gradients
+ * at long N).  It costs one more write of B*H*N*d bf16.  Errors as
+ * fa_fwd_blocksparse_gqa (without a mask: fa_fwd_gqa), plus FA_ERR_INVALID_ARG
+ * for an o_lo that is misaligned, overlaps another argument, or is given with
+ * dtype FA_F32.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, const unsigned char* block_mask, void* o, void* o_lo,
+              float* lse, int B, int H, int H_kv, int N, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * General backward: the gradients of the forward of fa_fwd_ex with the same
+ * block_mask (NULL: dense), H_kv, scale and causal; o, o_lo and lse from that
+ * call.  o_lo may be NULL: D is then formed from the bf16 o alone, exactly as
+ * fa_bwd does.  dq [B, H, N, d]; dk, dv [B, H_kv, N, d] (grouped heads summed in
+ * head order).  The workspace is sized by fa_bwd_gqa_workspace_size(); o_lo is
+ * read-only and must not overlap an output.  Arguments and errors otherwise as
+ * fa_bwd_blocksparse_gqa (without a mask: fa_bwd_gqa).
+ */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const unsigned char* block_mask, const void* o,
+              const void* o_lo, const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+              int H_kv, int N, int d, float scale, int causal, int dtype, int grad_dtype, void* workspace,
+              size_t workspace_bytes, void* stream);
+
 int fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsigned char* v,
                const float* q_scale, const float* k_scale, const float* v_scale, void* o, float* lse,
                int B, int H, int H_kv, int N, int d, float scale, int causal, void* stream);

@@ -35,39 +35,70 @@ def test_gpt2_small_workload_forward_backward():
     assert errs["dq"] <= TOL_BF16 and errs["dk"] <= TOL_BF16 and errs["dv"] <= TOL_BF16
 
 
-def test_long_16k_backward_full_heads():
-    """The 16K, d = 128 causal workload in the launch configuration the benchmark times (bf16
-    Q, K, V and dO, fp32 gradients, a caller-provided workspace): every element of dQ, dK and
-    dV of heads 0 and 15 against the oracle's backward of those heads.
+LONG_HEADS = (0, 15)
 
-    The gate is the oracle's per-element bound for bf16 arithmetic (oracle/bounds.py): P
-    rounded to bf16 for P.V and P^T dO, O stored in bf16 and used for D = <dO, O>, dS rounded
-    to bf16, everything else fp32.  At this size the gradients reach 6-9 in magnitude and
-    the errors exceed the flat 2e-2 that the smaller workloads meet: D formed from the
-    bf16-path O alone moves dK by about 0.02 here (the backward's error given the O it is
-    handed is about 0.015)."""
+
+@pytest.fixture(scope="module")
+def long_16k():
+    """The 16K, d = 128 causal workload (bf16 Q, K, V and dO) on the device, and the oracle's
+    gradients and bf16 error bounds of heads 0 and 15, computed once for the tests below."""
     w = inputs.WORKLOADS["long_s16k_d128"]
-    announce(w.name + " backward, heads 0 and 15")
     q, k, v, _ = inputs.make_qkv(w)
     do = inputs.draw(w.index, inputs.SLOT_DO, w.shape)
-    tq, tk, tv, tdo = dev(q, BF), dev(k, BF), dev(v, BF), dev(do, BF)
-    o, lse = api.forward(tq, tk, tv, w.scale, w.causal)
-    ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=tq.device)
-    dq, dk, dv = api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws)
-    torch.cuda.synchronize()
-    stats = {}
-    for h in (0, 15):
+    ref, bnd = {}, {}
+    for h in LONG_HEADS:
         sl = slice(h, h + 1)
         args = (q[:, sl], k[:, sl], v[:, sl], do[:, sl], w.scale, w.causal)
-        ref = oracle.backward(*args)
-        bnd = oracle.bf16_backward_bound(*args)
-        for name, g, r, e in zip(("dq", "dk", "dv"), (dq, dk, dv), ref, bnd):
+        ref[h] = oracle.backward(*args)
+        bnd[h] = oracle.bf16_backward_bound(*args)
+    return w, (dev(q, BF), dev(k, BF), dev(v, BF), dev(do, BF)), ref, bnd
+
+
+def _long_errors(w, grads, ref, bnd):
+    stats = {}
+    for h in LONG_HEADS:
+        sl = slice(h, h + 1)
+        for name, g, r, e in zip(("dq", "dk", "dv"), grads, ref[h], bnd[h]):
             err = np.abs(host(g[:, sl]) - r)
+            assert np.all(np.isfinite(err)), (name, h)
             stats[f"{name}_h{h}"] = float(err.max())
             stats[f"{name}_h{h}_over_bound"] = float((err / e).max())
-            assert np.all(np.isfinite(err)) and np.all(err <= e), (name, h, float((err / e).max()))
-        del ref, bnd
-    report(w.name + " backward", **stats)
+    return stats
+
+
+def test_long_16k_backward_full_heads(long_16k):
+    """The 16K, d = 128 causal workload in the launch configuration the benchmark times
+    (fa_fwd_ex writing o, lse and the low-order part o_lo; fa_bwd_ex with bf16 Q, K, V, dO,
+    fp32 gradients and a caller-provided workspace): every element of dQ, dK and dV of heads 0
+    and 15 within the bf16 tolerance of the oracle.  The per-element bf16 bound of
+    oracle/bounds.py is reported beside it as a diagnostic."""
+    w, (tq, tk, tv, tdo), ref, bnd = long_16k
+    announce(w.name + " backward with o_lo, heads 0 and 15")
+    o, lse, o_lo = api.forward_train(tq, tk, tv, w.scale, w.causal)
+    ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=tq.device)
+    grads = api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws, o_lo=o_lo)
+    torch.cuda.synchronize()
+    stats = _long_errors(w, grads, ref, bnd)
+    report(w.name + " backward (o_lo)", **stats)
+    for name in ("dq", "dk", "dv"):
+        for h in LONG_HEADS:
+            assert stats[f"{name}_h{h}"] <= TOL_BF16, (name, h, stats[f"{name}_h{h}"])
+
+
+def test_long_16k_backward_without_o_lo(long_16k):
+    """fa_bwd proper (D formed from the bf16 o alone) on the same heads.  At this size that
+    rounding of O moves dK by about 0.02 by itself, so the flat 2e-2 does not hold; the gate
+    here is the per-element bound of oracle/bounds.py, which includes O's rounding to bf16."""
+    w, (tq, tk, tv, tdo), ref, bnd = long_16k
+    announce(w.name + " backward without o_lo, heads 0 and 15")
+    o, lse = api.forward(tq, tk, tv, w.scale, w.causal)
+    grads = api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal)
+    torch.cuda.synchronize()
+    stats = _long_errors(w, grads, ref, bnd)
+    report(w.name + " backward (no o_lo)", **stats)
+    for name in ("dq", "dk", "dv"):
+        for h in LONG_HEADS:
+            assert stats[f"{name}_h{h}_over_bound"] <= 1.0, (name, h)
 
 
 @pytest.mark.parametrize("d", [64, 128])

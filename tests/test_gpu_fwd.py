@@ -170,3 +170,36 @@ def test_no_lse_and_guard_band():
     assert torch.all(buf[:1024] == 7.0) and torch.all(buf[1024 + n_el:] == 7.0)
     ro, _ = oracle.forward(q, k, v, 0.125, False)
     assert max_err(host(out), ro) <= TOL_BF16
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("masked", [False, True])
+def test_forward_train_low_order_part(d, causal, masked):
+    """fa_fwd_ex with o_lo: o is bitwise the plain forward's, |o_lo| is at most half an ulp of
+    o (o is O rounded to nearest), and o + o_lo is closer to the oracle than o alone.  What
+    remains in o + o_lo is the rounding of P to bf16 for the P.V product (about 5e-3 at this
+    logit spread), so the gate is half the bf16 tolerance."""
+    n = 1030
+    announce(f"fwd_ex o_lo N={n} d={d} causal={causal} masked={masked}")
+    q, k, v, _ = inputs.random_case(31, 1, 3, n, d, "bf16", mult=1.5)
+    scale = api.default_scale(d)
+    tq, tk, tv = dev(q, BF), dev(k, BF), dev(v, BF)
+    mask = None
+    if masked:
+        mask_np = inputs.random_block_mask(31, -(-n // 128), 0.4, causal)
+        mask = torch.from_numpy(mask_np).to(tq.device)
+        o_ref, lse_ref = api.forward_blocksparse(tq, tk, tv, mask, scale, causal)
+        ro, rl = oracle.forward(q, k, v, scale, causal, block_mask=mask_np)
+    else:
+        o_ref, lse_ref = api.forward(tq, tk, tv, scale, causal)
+        ro, rl = oracle.forward(q, k, v, scale, causal)
+    o, lse, o_lo = api.forward_train(tq, tk, tv, scale, causal, block_mask=mask)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+    ho, hl = host(o), host(o_lo)
+    ulp = np.spacing(np.abs(ho).astype(np.float32)).astype(np.float64) * 2.0 ** 16  # bf16 ulp of o
+    assert np.all(np.abs(hl) <= 0.5 * ulp + 1e-30)
+    e_hi, e_full = max_err(ho, ro), max_err(ho + hl, ro)
+    report(f"o_lo d={d} causal={causal} masked={masked}", o=e_hi, o_plus_lo=e_full)
+    assert e_full <= e_hi and e_full <= TOL_BF16 / 2
