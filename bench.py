@@ -145,14 +145,14 @@ def kernel_table():
             tm = torch.from_numpy(mask).to("cuda:0")
             ms = time_calls(lambda: api.forward_blocksparse(tq, tk, tv, tm, w.scale, w.causal), 10)
             entry.update(fwd_ms=ms, fwd_tflops=flops_fwd(w, dens) / ms / 1e9, density=dens)
-            # block-sparse backward on the same mask
-            o, lse = api.forward_blocksparse(tq, tk, tv, tm, w.scale, w.causal)
+            # block-sparse backward on the same mask (D formed from o + o_lo, as in training)
+            o, lse, o_lo = api.forward_train(tq, tk, tv, w.scale, w.causal, block_mask=tm)
             tdo = to_dev(inputs.draw(w.index, inputs.SLOT_DO, w.shape), torch.bfloat16)
             ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda:0")
             bms = time_calls(lambda: api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws,
-                                                  block_mask=tm), 5)
+                                                  block_mask=tm, o_lo=o_lo), 5)
             entry.update(bwd_ms=bms, bwd_tflops=2.5 * flops_fwd(w, dens) / bms / 1e9)
-            del o, lse, tdo, ws
+            del o, lse, o_lo, tdo, ws
         else:
             ms = time_calls(lambda: api.forward(tq, tk, tv, w.scale, w.causal), 20)
             entry.update(fwd_ms=ms, fwd_tflops=flops_fwd(w) / ms / 1e9)
@@ -183,11 +183,12 @@ def kernel_table():
                 entry.update(fwd_graph_ms=gms, fwd_graph_tflops=flops_fwd(w) / gms / 1e9)
                 del graph, o_g, l_g
             if w.backward or w.name == "long_s16k_d128" or w.Hkv is not None:
-                o, lse = api.forward(tq, tk, tv, w.scale, w.causal)
+                o, lse, o_lo = api.forward_train(tq, tk, tv, w.scale, w.causal)
                 tdo = to_dev(inputs.draw(w.index, inputs.SLOT_DO, w.shape), torch.bfloat16)
                 ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d, H_kv=w.kv_heads), dtype=torch.uint8,
                                  device="cuda:0")
-                bms = time_calls(lambda: api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws), 10)
+                bms = time_calls(lambda: api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws,
+                                                      o_lo=o_lo), 10)
                 entry.update(bwd_ms=bms, bwd_tflops=2.5 * flops_fwd(w) / bms / 1e9)
         entry["fwd_frac_peak"] = entry["fwd_tflops"] / PEAK_BF16_TFLOPS
         rows[name] = {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in entry.items()}

@@ -18,6 +18,10 @@ from . import _lib
 _DTYPES = {torch.float32: _lib.FA_F32, torch.bfloat16: _lib.FA_BF16}
 
 
+def _on_gpu(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
 def _stream_ptr(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -34,7 +38,7 @@ def _check_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, allow_gqa: boo
     if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype bfloat16 or float32")
     for t in (q, k, v):
-        if not t.is_cuda or t.device != q.device:
+        if not _on_gpu(t) or t.device != q.device:
             raise ValueError("q, k, v must be on the same GPU")
         if not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous")
@@ -286,7 +290,7 @@ def quantize_fp8(x: torch.Tensor, signs: Optional[torch.Tensor] = None) -> Tuple
     randomised Hadamard transform first (incoherent processing; use the same signs
     for Q and K and none for V).
     """
-    if x.dim() != 4 or x.dtype not in _DTYPES or not x.is_cuda or not x.is_contiguous():
+    if x.dim() != 4 or x.dtype not in _DTYPES or not _on_gpu(x) or not x.is_contiguous():
         raise ValueError("x must be a contiguous [B, H, N, d] bf16 or float32 GPU tensor")
     B, H, N, d = x.shape
     if signs is not None:
@@ -311,7 +315,7 @@ def forward_fp8(q8: torch.Tensor, q_scale: torch.Tensor, k8: torch.Tensor, k_sca
     k8, v8 may have H_kv | H heads (grouped-query).
     """
     for t in (q8, k8, v8):
-        if t.dim() != 4 or t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous() or t.device != q8.device:
+        if t.dim() != 4 or t.dtype != torch.uint8 or not _on_gpu(t) or not t.is_contiguous() or t.device != q8.device:
             raise ValueError("q8, k8, v8 must be contiguous uint8 [B, H, N, d] tensors on one GPU")
     B, H, N, d = q8.shape
     hkv = k8.shape[1]

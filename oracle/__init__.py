@@ -20,6 +20,8 @@ Parity status of each function (how it is pinned, in tests/test_oracle_*.py):
   forward / forward_rows      -- brute force, closed forms, torch fp64 SDPA, golden hand cases
   forward_blockwise / merge   -- equals the one-shot forward; the dropped-l mutation fails
   backward                    -- central finite differences, torch fp64 autograd, invariants
+  backward_rows               -- equals `backward` on the sampled rows and keys (dense, causal,
+                                 block-sparse, grouped heads) and torch fp64 autograd
   grouped-/multi-query heads  -- torch fp64 SDPA and autograd with enable_gqa, brute force and
                                  finite differences, K/V heads repeated == plain multi-head
   bf16_backward_bound         -- holds for a step-by-step simulation of a bf16 kernel's roundings,
@@ -32,6 +34,7 @@ Parity status of each function (how it is pinned, in tests/test_oracle_*.py):
 from .attention import (  # noqa: F401
     allowed,
     backward,
+    backward_rows,
     forward,
     forward_blockwise,
     forward_rows,

@@ -263,3 +263,74 @@ def backward(q, k, v, do, scale, causal=False, block_mask=None, mask_block=128, 
     if return_delta:
         return dq, dk, dv, delta
     return dq, dk, dv
+
+
+def _row_groups(rows, block_mask, mask_block, chunk):
+    """Consecutive pieces of the sorted `rows`: one mask row at a time when there is a block
+    mask (so only the keys it keeps are touched), else `chunk` rows at a time."""
+    if rows.size == 0:
+        return []
+    if block_mask is None:
+        return [rows[i:i + chunk] for i in range(0, rows.size, chunk)]
+    cut = np.nonzero(np.diff(rows // mask_block))[0] + 1
+    return np.split(rows, cut)
+
+
+def backward_rows(q, k, v, do, scale, causal=False, block_mask=None, mask_block=128, rows=None, keys=None,
+                  heads=None, chunk=512):
+    """Part of the backward of `backward`, for checks at sizes where all of it is too slow.
+
+    Returns (dq [B, H, R, d] of the query rows `rows`, dk and dv [B, H_kv, K, d] of the
+    keys `keys`) in float64, with the same chain rule as `backward`:
+    dV_j = sum_i P_ij dO_i, dK_j = scale sum_i dS_ij q_i, dQ_i = scale sum_j dS_ij k_j,
+    dS_ij = P_ij (dP_ij - D_i), dP_ij = <dO_i, v_j>, D_i = <dO_i, O_i>.
+    A key's gradient sums over every query that sees it, so the statistics (the row's
+    softmax and D_i) are computed for all of those rows, not only the sampled ones.
+    `heads`: optional list of the K/V heads (b, h_kv) to evaluate (all by default); the
+    entries of the others stay zero, and dq is filled for their query heads only.
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, N, d = q.shape
+    hkv = k.shape[1]
+    rows = np.unique(np.asarray([] if rows is None else rows, dtype=np.int64))
+    keys = np.unique(np.asarray([] if keys is None else keys, dtype=np.int64))
+    dq = np.zeros((B, H, rows.size, d))
+    dk = np.zeros((B, hkv, keys.size, d))
+    dv = np.zeros((B, hkv, keys.size, d))
+    g = H // hkv
+    todo = [(b, j) for b in range(B) for j in range(hkv)] if heads is None else list(heads)
+    # rows that see at least one sampled key, plus the sampled rows themselves
+    if keys.size:
+        sees = allowed(np.arange(N), N, causal, block_mask, mask_block, cols=keys).any(axis=1)
+    else:
+        sees = np.zeros(N, dtype=bool)
+    sees[rows] = True
+    need = np.nonzero(sees)[0]
+    row_pos = {int(r): i for i, r in enumerate(rows)}
+    for b, kh in todo:
+        K, V = k[b, kh], v[b, kh]
+        for h in range(kh * g, (kh + 1) * g):
+            if kv_head(h, H, hkv) != kh:
+                raise AssertionError("query head outside its K/V group")
+            for grp in _row_groups(need, block_mask, mask_block, chunk):
+                cols = _visible_columns(grp, N, causal, block_mask, mask_block)
+                if cols.size == 0:
+                    continue
+                Q, dO = q[b, h, grp], do[b, h, grp]
+                ok = allowed(grp, N, causal, block_mask, mask_block, cols=cols)
+                P = _probs_one_head(Q, K[cols], ok, scale)
+                D = np.sum(dO * (P @ V[cols]), axis=1)
+                # dQ of the sampled rows in this piece
+                sel = np.array([i for i, r in enumerate(grp) if int(r) in row_pos], dtype=np.int64)
+                if sel.size:
+                    dS = P[sel] * (dO[sel] @ V[cols].T - D[sel, None])
+                    dq[b, h, [row_pos[int(r)] for r in grp[sel]]] = scale * (dS @ K[cols])
+                # dK, dV of the sampled keys this piece sees
+                kin = np.nonzero(np.isin(keys, cols))[0]
+                if kin.size:
+                    at = np.searchsorted(cols, keys[kin])
+                    Pk = P[:, at]
+                    dSk = Pk * (dO @ V[keys[kin]].T - D[:, None])
+                    dv[b, kh, kin] += Pk.T @ dO
+                    dk[b, kh, kin] += scale * (dSk.T @ Q)
+    return dq, dk, dv

@@ -417,6 +417,46 @@ def check_gqa_backward(seed=14):
                 assert np.max(np.abs(a - r.reshape(2, hkv, g, 19, 6).sum(axis=2))) <= 1e-12
 
 
+def check_backward_rows(seed=17):
+    """The sampled backward (dQ of some rows, dK/dV of some keys) equals the full backward at
+    those rows and keys -- dense and causal, with a block mask (tile 4), with grouped heads,
+    ragged lengths, empty row or key sets -- and equals torch fp64 autograd on a grouped case."""
+    import torch
+
+    cases = ((1, 2, 2, 23, 3, False, False), (2, 4, 2, 30, 4, True, False), (1, 3, 1, 29, 2, True, True),
+             (2, 2, 2, 17, 5, False, True), (1, 4, 4, 1, 3, True, False))
+    for i, (B, H, hkv, N, d, causal, masked) in enumerate(cases):
+        q, do = _rand(seed + 10 * i, (B, H, N, d)), _rand(seed + 10 * i + 1, (B, H, N, d))
+        k, v = _rand(seed + 10 * i + 2, (B, hkv, N, d)), _rand(seed + 10 * i + 3, (B, hkv, N, d))
+        mb = 4
+        mask = None
+        if masked:
+            nb = -(-N // mb)
+            mask = (np.random.default_rng(seed + i).random((nb, nb)) < 0.5).astype(np.uint8)
+            mask[nb // 2, :] = 0  # a mask row with no visible key
+        full = oracle.backward(q, k, v, do, 0.6, causal, block_mask=mask, mask_block=mb)
+        rng = np.random.default_rng(seed + 100 + i)
+        for rows, keys in ((rng.choice(N, min(N, 7), replace=False), rng.choice(N, min(N, 6), replace=False)),
+                           ([], np.arange(N)), (np.arange(N), [])):
+            got = oracle.backward_rows(q, k, v, do, 0.6, causal, block_mask=mask, mask_block=mb, rows=rows,
+                                       keys=keys, chunk=5)
+            r, c = np.unique(np.asarray(rows, dtype=np.int64)), np.unique(np.asarray(keys, dtype=np.int64))
+            assert np.max(np.abs(got[0] - full[0][:, :, r]), initial=0.0) <= 1e-12, (i, "dq")
+            assert np.max(np.abs(got[1] - full[1][:, :, c]), initial=0.0) <= 1e-12, (i, "dk")
+            assert np.max(np.abs(got[2] - full[2][:, :, c]), initial=0.0) <= 1e-12, (i, "dv")
+    q, do = _rand(seed + 90, (1, 4, 26, 5)), _rand(seed + 91, (1, 4, 26, 5))
+    k, v = _rand(seed + 92, (1, 2, 26, 5)), _rand(seed + 93, (1, 2, 26, 5))
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=0.45, enable_gqa=True)
+    (out * torch.from_numpy(do)).sum().backward()
+    rows, keys = [0, 3, 11, 25], [0, 1, 12, 25]
+    got = oracle.backward_rows(q, k, v, do, 0.45, True, rows=rows, keys=keys, heads=[(0, 1)])
+    assert np.max(np.abs(got[0][:, 2:] - tq.grad.numpy()[:, 2:, rows])) <= 1e-12
+    assert np.max(np.abs(got[0][:, :2])) == 0.0  # query heads of K/V head 0 were not asked for
+    assert np.max(np.abs(got[1][:, 1] - tk.grad.numpy()[:, 1, keys])) <= 1e-12
+    assert np.max(np.abs(got[2][:, 1] - tv.grad.numpy()[:, 1, keys])) <= 1e-12
+
+
 def _bf16(x):
     import torch
 
@@ -471,6 +511,7 @@ def check_bf16_backward_bound(seed=16):
 
 
 BACKWARD_CHECKS = [
+    check_backward_rows,
     check_bf16_backward_bound,
     check_finite_differences,
     check_torch_autograd,

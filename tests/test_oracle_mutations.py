@@ -116,6 +116,19 @@ def _backward_group_not_summed(q, k, v, do, scale, causal=False, block_mask=None
 
 
 _orig_backward = oatt.backward
+_orig_backward_rows = oatt.backward_rows
+
+
+def _backward_rows_sampled_queries_only(q, k, v, do, scale, causal=False, block_mask=None, mask_block=128,
+                                        rows=None, keys=None, heads=None, chunk=512):
+    """dK/dV of the sampled keys summed over the sampled query rows only (not every row that sees
+    them): dO zeroed outside the sampled rows, which leaves their dQ as it was."""
+    rows = np.unique(np.asarray([] if rows is None else rows, dtype=np.int64))
+    keep = np.zeros(np.shape(q)[2], dtype=bool)
+    keep[rows] = True
+    do = np.where(keep[None, None, :, None], np.asarray(do, dtype=np.float64), 0.0)
+    return _orig_backward_rows(q, k, v, do, scale, causal, block_mask, mask_block, rows, keys, heads, chunk)
+
 
 MUTATIONS = {
     "lse_without_max": ("_rows_one_head", _rows_no_max_shift_in_lse, pins.FORWARD_CHECKS),
@@ -130,6 +143,8 @@ MUTATIONS = {
     "delta_dropped": ("backward", _backward_delta_dropped, pins.BACKWARD_CHECKS),
     "kv_heads_interleaved": ("kv_head", _kv_head_interleaved, pins.ALL_CHECKS),
     "gqa_grads_not_summed": ("backward", _backward_group_not_summed, pins.BACKWARD_CHECKS),
+    "sampled_keys_see_sampled_rows_only": ("backward_rows", _backward_rows_sampled_queries_only,
+                                           [pins.check_backward_rows]),
 }
 
 
