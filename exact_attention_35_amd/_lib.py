@@ -16,15 +16,17 @@ FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_WORKSPACE = -3
 FA_ERR_HIP = -4
+FA_ERR_SCRATCH = -5
 FA_F32 = 0
 FA_BF16 = 1
 FA_MASK_BLOCK = 128
 FA_FP8_BLOCK = 128
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
 FA_ABI_VERSION = 5  # must equal FA_ABI_VERSION of include/fa.h
 
 EXPORTS = ("fa_fwd", "fa_fwd_gqa", "fa_fwd_blocksparse", "fa_bwd_workspace_size", "fa_bwd",
            "fa_bwd_gqa_workspace_size", "fa_bwd_gqa", "fa_bwd_blocksparse", "fa_fwd_blocksparse_gqa",
-           "fa_bwd_blocksparse_gqa", "fa_fwd_ex", "fa_bwd_ex", "fa_quantize_fp8", "fa_fwd_fp8",
+           "fa_bwd_blocksparse_gqa", "fa_fwd_ex", "fa_bwd_ex", "fa_bwd_noalloc", "fa_quantize_fp8", "fa_fwd_fp8",
            "fa_status_string", "fa_version")
 
 _lib = None
@@ -89,6 +91,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_ex.argtypes = [_vp] * 7 + [_i] * 5 + [_f, _i, _i, _vp]
     lib.fa_bwd_ex.restype = _i
     lib.fa_bwd_ex.argtypes = [_vp] * 11 + [_i] * 5 + [_f, _i, _i, _i, _vp, ctypes.c_size_t, _vp]
+    lib.fa_bwd_noalloc.restype = _i
+    lib.fa_bwd_noalloc.argtypes = [_vp] * 11 + [_i] * 5 + [_f, _i, _i, _i, _vp]
     _lib = lib
     return lib
 

@@ -248,6 +248,42 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     return dq, dk, dv
 
 
+def backward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                     do: torch.Tensor, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
+                     scale: Optional[float] = None, causal: bool = False, block_mask: Optional[torch.Tensor] = None,
+                     o_lo: Optional[torch.Tensor] = None) -> None:
+    """fa_bwd_noalloc: the backward into caller-given dq, dk, dv (fp32 or bf16, all one dtype)
+    with the library's static device workspace instead of a caller workspace; nothing is
+    allocated, so it may be captured in a HIP graph.  Calls that overlap on one GPU race on
+    that workspace.  Arguments otherwise as backward()."""
+    B, H, N, d = _check_qkv(q, k, v, allow_gqa=True)
+    hkv = k.shape[1]
+    if block_mask is not None:
+        _check_mask(block_mask, N, q.device)
+    for name, t in (("o", o), ("do", do)):
+        _check_buffer(t, q.shape, q.dtype, q.device, name)
+    _check_buffer(lse, (B, H, N), torch.float32, q.device, "lse")
+    if o_lo is not None:
+        if q.dtype != torch.bfloat16:
+            raise ValueError("o_lo applies to bfloat16 inputs only")
+        _check_buffer(o_lo, q.shape, q.dtype, q.device, "o_lo")
+    grad_dtype = dq.dtype if isinstance(dq, torch.Tensor) else None
+    if grad_dtype not in _DTYPES:
+        raise ValueError("dq must be a float32 or bfloat16 tensor")
+    _check_buffer(dq, q.shape, grad_dtype, q.device, "dq")
+    _check_buffer(dk, k.shape, grad_dtype, q.device, "dk")
+    _check_buffer(dv, k.shape, grad_dtype, q.device, "dv")
+    scale = default_scale(d) if scale is None else float(scale)
+    lib = _lib.load()
+    with torch.cuda.device(q.device):
+        st = lib.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                None if block_mask is None else block_mask.data_ptr(), o.data_ptr(),
+                                None if o_lo is None else o_lo.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, hkv, N, d, scale,
+                                int(bool(causal)), _DTYPES[q.dtype], _DTYPES[grad_dtype], _stream_ptr(q.device))
+    _lib.check(st, "fa_bwd_noalloc")
+
+
 class FlashAttentionFunction(torch.autograd.Function):
     """autograd wrapper: forward (fa_fwd_ex) saves q, k, v, o, lse, the low-order part of o
     (bf16 inputs) and the block mask; backward calls fa_bwd_ex with them (fp32 inputs: fa_bwd

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "fa_launch.hpp"
 
 namespace {
@@ -124,6 +126,9 @@ const char* fa_status_string(int status) {
       return "FA_ERR_WORKSPACE: workspace missing or smaller than fa_bwd_workspace_size()";
     case FA_ERR_HIP:
       return "FA_ERR_HIP: a HIP kernel launch failed";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: fa_bwd_noalloc needs more workspace than its static device buffer holds "
+             "(FA_NOALLOC_SCRATCH_BYTES = 32 MiB); use fa_bwd_ex with a caller workspace";
     default:
       return "unknown status";
   }
@@ -176,10 +181,35 @@ namespace {
 constexpr size_t bwd_dkdv_static_lds(int d) { return d == 128 ? 132608 + 64 : 83456 + 64; }
 constexpr size_t kBwdDqStaticLds = (size_t)6 * 16384 + 256;
 
+// ---- the static workspace of fa_bwd_noalloc: one array per GPU, alive until the process ends.
+// In host code `scratch` only names the variable; its device address on the current GPU comes
+// from hipGetSymbolAddress, taken once per device and kept.
+constexpr size_t kScratchBytes = (size_t)FA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current GPU's scratch array, or null on a HIP error.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// use_scratch: the workspace is the static scratch array (workspace and workspace_bytes are
+// ignored); checked against its size, and its address taken only after every other check.
 int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* mask, const void* o, const void* o_lo,
              const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
              float scale, int causal, int dtype, int grad_dtype, void* workspace, size_t workspace_bytes,
-             void* stream, bool sparse) {
+             void* stream, bool sparse, bool use_scratch = false) {
   int st = check_common(B, H, N, d, scale, causal, dtype);
   if (st != FA_OK) return st;
   if (!valid_kv_heads(H, Hkv)) return FA_ERR_INVALID_ARG;
@@ -199,8 +229,13 @@ int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* m
     if (kBwdDqStaticLds + ((nb * 4 + 15) & ~(size_t)15) > kLdsBytes) return FA_ERR_UNSUPPORTED;
   }
   const size_t need = fa_bwd_gqa_workspace_size(B, H, Hkv, N, d, grad_dtype);
-  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  if (use_scratch) {
+    if (need > kScratchBytes) return FA_ERR_SCRATCH;
+    workspace = nullptr;  // its range (below) is empty: the static array is no caller buffer
+  } else {
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  }
   const size_t n = (size_t)B * H * N;
   const size_t nkv = (size_t)B * Hkv * N;
   const size_t tb = n * d * elem_bytes(dtype);
@@ -210,7 +245,8 @@ int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* m
   const Range ins[7] = {range_of(q, tb),      range_of(k, kvb), range_of(v, kvb),
                         range_of(o, tb),      range_of(lse, n * 4), range_of(dO, tb),
                         range_of(o_lo, o_lo ? tb : 0)};
-  const Range outs[4] = {range_of(dq, gb), range_of(dk, gkvb), range_of(dv, gkvb), range_of(workspace, need)};
+  const Range outs[4] = {range_of(dq, gb), range_of(dk, gkvb), range_of(dv, gkvb),
+                         range_of(workspace, workspace ? need : 0)};
   for (int i = 0; i < 4; ++i) {
     for (const Range& r : ins)
       if (overlap(outs[i], r)) return FA_ERR_INVALID_ARG;
@@ -220,6 +256,10 @@ int bwd_impl(const void* q, const void* k, const void* v, const unsigned char* m
       const size_t nb = ((size_t)N + FA_MASK_BLOCK - 1) / FA_MASK_BLOCK;
       if (overlap(outs[i], range_of(mask, nb * nb))) return FA_ERR_INVALID_ARG;
     }
+  }
+  if (use_scratch) {
+    workspace = scratch_on_current_device();
+    if (workspace == nullptr) return FA_ERR_HIP;
   }
   fa::BwdParams p;
   p.q = q;
@@ -294,6 +334,13 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const unsigned char* 
               size_t workspace_bytes, void* stream) {
   return bwd_impl(q, k, v, block_mask, o, o_lo, lse, dO, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype,
                   grad_dtype, workspace, workspace_bytes, stream, block_mask != nullptr);
+}
+
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const unsigned char* block_mask, const void* o,
+                   const void* o_lo, const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+                   int H_kv, int N, int d, float scale, int causal, int dtype, int grad_dtype, void* stream) {
+  return bwd_impl(q, k, v, block_mask, o, o_lo, lse, dO, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype,
+                  grad_dtype, nullptr, 0, stream, block_mask != nullptr, /*use_scratch=*/true);
 }
 
 }  // extern "C"

@@ -49,6 +49,7 @@ extern "C" {
 #define FA_ABI_VERSION 5
 #define FA_MASK_BLOCK 128 /* rows and keys covered by one block-sparse mask entry */
 #define FA_FP8_BLOCK 128  /* rows of one head that share one fp8 scale */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20) /* static workspace of fa_bwd_noalloc, per GPU */
 
 enum fa_status {
   FA_OK = 0,
@@ -61,7 +62,8 @@ enum fa_status {
                               (N above about 2.09M); bf16 gradients for
                               fp32 inputs */
   FA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than fa_bwd_workspace_size() */
-  FA_ERR_HIP = -4          /* a HIP launch reported an error */
+  FA_ERR_HIP = -4,         /* a HIP launch reported an error */
+  FA_ERR_SCRATCH = -5      /* fa_bwd_noalloc: the call needs more than FA_NOALLOC_SCRATCH_BYTES */
 };
 
 enum fa_dtype { FA_F32 = 0, FA_BF16 = 1 };
@@ -251,6 +253,29 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const unsigned char* 
               const void* o_lo, const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
               int H_kv, int N, int d, float scale, int causal, int dtype, int grad_dtype, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/*
+ * Backward that allocates nothing and takes no workspace: fa_bwd_ex with the
+ * workspace replaced by a static device array of FA_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) inside the library, one per GPU, held from the first call on that
+ * GPU until the process ends.  For callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the call makes no hipMalloc or hipFree and no allocating library
+ * call; the caller still passes every input and output.  The calls that fit are
+ * those whose fa_bwd_gqa_workspace_size() is at most FA_NOALLOC_SCRATCH_BYTES
+ * (without grouped heads: B*H*N <= 4194304 rows); larger ones return
+ * FA_ERR_SCRATCH before any GPU work.  The array belongs to the GPU that is
+ * current at the call (the stream and the buffers must be on it); its address
+ * is looked up on the first call on each GPU.  Every call on one GPU uses the
+ * same array and leaves its contents there (nothing in it needs clearing: each
+ * call writes every workspace entry it reads before reading it), so calls
+ * that overlap on one GPU -- on two streams, or from two threads without
+ * ordering -- race on it and must not be made.  Arguments, results and other
+ * errors as fa_bwd_ex; results are bitwise those of fa_bwd_ex.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const unsigned char* block_mask, const void* o,
+                   const void* o_lo, const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H,
+                   int H_kv, int N, int d, float scale, int causal, int dtype, int grad_dtype, void* stream);
 
 int fa_fwd_fp8(const unsigned char* q, const unsigned char* k, const unsigned char* v,
                const float* q_scale, const float* k_scale, const float* v_scale, void* o, float* lse,

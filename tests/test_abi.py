@@ -216,3 +216,23 @@ def test_fp8_validation(lib):
     assert h(q, k, v, qs, ks, vs, q + 32, lse, 1, 4, 2, 256, 64, 0.1, 1, None) == INV  # o overlaps q
     assert h(q, k, v, qs, ks, vs, o, o + 16, 1, 4, 2, 256, 64, 0.1, 1, None) == INV    # lse inside o
     assert h(q, k, v, qs + 1, ks, vs, o, lse, 1, 4, 2, 256, 64, 0.1, 1, None) == INV  # misaligned scale
+
+
+def noalloc(lib, B=1, H=2, Hkv=2, N=64, d=64, q=P, grad_dtype=0):
+    p = [q] + [P + i * MB for i in range(1, 11)]
+    return lib.fa_bwd_noalloc(p[0], p[1], p[2], None, p[3], None, p[4], p[5], p[6], p[7], p[8], B, H, Hkv, N, d,
+                              0.125, 1, 1, grad_dtype, None)
+
+
+def test_noalloc_rejects_what_its_static_workspace_cannot_hold(lib):
+    """fa_bwd_noalloc checks its arguments, then the workspace it needs against the static
+    array, all before any HIP call (fake pointers; no GPU is used)."""
+    assert noalloc(lib, q=None) == INV
+    assert noalloc(lib, d=96) == UNS
+    rows_max = _lib.FA_NOALLOC_SCRATCH_BYTES // 8
+    assert noalloc(lib, B=1, H=64, N=rows_max // 64 + 1) == _lib.FA_ERR_SCRATCH
+    assert noalloc(lib, B=2, H=8, N=rows_max // 16 + 1) == _lib.FA_ERR_SCRATCH
+    # grouped heads keep fp32 per-head dK/dV partials in the workspace as well
+    assert noalloc(lib, B=1, H=8, Hkv=1, N=8192, d=128) == _lib.FA_ERR_SCRATCH
+    assert lib.fa_bwd_gqa_workspace_size(1, 8, 1, 8192, 128, 0) > _lib.FA_NOALLOC_SCRATCH_BYTES
+    assert _lib.status_string(_lib.FA_ERR_SCRATCH).startswith("FA_ERR_SCRATCH")
