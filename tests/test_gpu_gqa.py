@@ -241,3 +241,38 @@ def test_gqa_workload_full_size():
     del tq, tk, tv, o, lse
     torch.cuda.empty_cache()
     _repeat_equivalence(w.B, w.H, w.kv_heads, w.N, w.d, w.causal, 35)
+
+
+def test_gqa_workload_backward_sampled():
+    """The grouped-query 16K workload's backward in the launch configuration the benchmark
+    times (fa_fwd_ex with o_lo, then fa_bwd_ex; fp32 gradients): dQ of 256 sampled rows of
+    the query heads of K/V heads 0 and 7, and dK, dV of 256 sampled keys of those two K/V
+    heads (each the sum over its four query heads and every query that sees the key),
+    against the oracle's sampled backward."""
+    w = inputs.WORKLOADS["gqa_s16k_h32_kv8_d128"]
+    announce(w.name + " backward, sampled rows and keys of K/V heads 0 and 7")
+    q, k, v, _ = inputs.make_qkv(w)
+    do = inputs.draw(w.index, inputs.SLOT_DO, w.shape)
+    tq, tk, tv, tdo = dev(q, BF), dev(k, BF), dev(v, BF), dev(do, BF)
+    o, lse, o_lo = api.forward_train(tq, tk, tv, w.scale, w.causal)
+    ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d, H_kv=w.kv_heads), dtype=torch.uint8,
+                     device=tq.device)
+    dq, dk, dv = api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws, o_lo=o_lo)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(w.N, w.sample_rows, w.index)
+    keys = inputs.sample_rows(w.N, w.sample_rows, w.index, head=1)
+    ri, ki = torch.from_numpy(rows).to(tq.device), torch.from_numpy(keys).to(tq.device)
+    gq, gk, gv = host(dq[:, :, ri]), host(dk[:, :, ki]), host(dv[:, :, ki])
+    g = w.H // w.kv_heads
+    errs = {}
+    for kh in (0, 7):
+        qs, ks = slice(kh * g, (kh + 1) * g), slice(kh, kh + 1)
+        rq, rk, rv = oracle.backward_rows(q[:, qs], k[:, ks], v[:, ks], do[:, qs], w.scale, w.causal,
+                                          rows=rows, keys=keys)
+        errs[f"dq_kv{kh}"] = max_err(gq[:, qs], rq)
+        errs[f"dk_kv{kh}"] = max_err(gk[:, ks], rk)
+        errs[f"dv_kv{kh}"] = max_err(gv[:, ks], rv)
+    report(w.name + " backward", **errs)
+    assert all(e <= TOL_BF16 for n, e in errs.items() if n.startswith("dq")), errs
+    # dK, dV of a shared head add g per-head gradients whose rounding errors are independent
+    assert all(e <= TOL_BF16 * np.sqrt(g) for n, e in errs.items() if not n.startswith("dq")), errs

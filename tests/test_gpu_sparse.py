@@ -170,3 +170,38 @@ def test_autograd_wrapper_with_block_mask():
     rq, rk, rv = oracle.backward(q, k, v, do, scale, True, mask, inputs.MASK_BLOCK)
     for g, r in ((tq.grad, rq), (tk.grad, rk), (tv.grad, rv)):
         assert max_err(host(g), r) <= 2 * TOL_BF16
+
+
+def test_blocksparse_64k_backward_sampled():
+    """The block-sparse 64K workload's backward in the launch configuration the benchmark times
+    (fa_fwd_ex with o_lo, then fa_bwd_ex with the mask; fp32 gradients): dQ of 256 sampled query
+    rows and dK, dV of 256 sampled keys (the boundary rows and keys included) of four heads
+    against the oracle's sampled backward, which sums each key's gradient over every query
+    that sees it."""
+    w = inputs.WORKLOADS["blocksparse_s64k"]
+    announce(w.name + " backward, sampled rows and keys of four heads")
+    q, k, v, _ = inputs.make_qkv(w)
+    do = inputs.draw(w.index, inputs.SLOT_DO, w.shape)
+    nb = w.N // inputs.MASK_BLOCK
+    mask = inputs.make_block_mask(nb, w.density, w.index, causal=w.causal)
+    tq, tk, tv, tdo = dev(q, BF), dev(k, BF), dev(v, BF), dev(do, BF)
+    tm = torch.from_numpy(mask).to(tq.device)
+    o, lse, o_lo = api.forward_train(tq, tk, tv, w.scale, w.causal, block_mask=tm)
+    ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=tq.device)
+    dq, dk, dv = api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws, block_mask=tm, o_lo=o_lo)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(w.N, w.sample_rows, w.index)
+    keys = inputs.sample_rows(w.N, w.sample_rows, w.index, head=1)
+    ri, ki = torch.from_numpy(rows).to(tq.device), torch.from_numpy(keys).to(tq.device)
+    gq, gk, gv = host(dq[:, :, ri]), host(dk[:, :, ki]), host(dv[:, :, ki])
+    assert np.all(np.isfinite(gq)) and np.all(np.isfinite(gk)) and np.all(np.isfinite(gv))
+    errs = {}
+    for b, h in ((0, 0), (0, 9), (1, 6), (1, 15)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = oracle.backward_rows(q[sl], k[sl], v[sl], do[sl], w.scale, w.causal, mask, inputs.MASK_BLOCK,
+                                          rows=rows, keys=keys)
+        errs[f"dq_{b}{h}"] = max_err(gq[sl], rq)
+        errs[f"dk_{b}{h}"] = max_err(gk[sl], rk)
+        errs[f"dv_{b}{h}"] = max_err(gv[sl], rv)
+    report(w.name + " backward", **errs)
+    assert max(errs.values()) <= TOL_BF16, errs
