@@ -159,3 +159,26 @@ def test_grouped_query_workspace_must_hold_the_partials():
     gqa_need = FakeLib().fa_bwd_gqa_workspace_size(B, H, 1, N, D, 0)
     with pytest.raises(LibCalled):
         api.backward(q, k, v, o, lse, do, workspace=torch.empty(gqa_need, dtype=torch.uint8))
+
+
+def test_grouped_query_shapes_never_reach_the_dense_entry_points():
+    """K and V with H_kv < H heads hold B*H_kv*N*d elements; the dense fa_fwd / fa_bwd read
+    B*H*N*d of each and would run past them.  The binding sends such shapes to the _gqa entry
+    points, and refuses a head count that does not divide H, before any library call."""
+    q, k, v = qkv(heads_kv=1)
+    o, lse, do = torch.zeros_like(q), torch.zeros(B, H, N), torch.zeros_like(q)
+    with pytest.raises(LibCalled, match="^fa_fwd_gqa$"):
+        api.forward(q, k, v)
+    mask = torch.ones(1, 1, dtype=torch.uint8)
+    with pytest.raises(LibCalled, match="^fa_fwd_blocksparse_gqa$"):
+        api.forward_blocksparse(q, k, v, mask)
+    with pytest.raises(LibCalled, match="^fa_bwd_gqa$"):
+        api.backward(q, k, v, o, lse, do)
+    with pytest.raises(LibCalled, match="^fa_bwd_blocksparse_gqa$"):
+        api.backward(q, k, v, o, lse, do, block_mask=mask)
+    q3 = torch.zeros(B, 3, N, D, dtype=BF)
+    k2, v2 = torch.zeros(B, 2, N, D, dtype=BF), torch.zeros(B, 2, N, D, dtype=BF)
+    with pytest.raises(ValueError):
+        api.forward(q3, k2, v2)
+    with pytest.raises(ValueError):
+        api.backward(q3, k2, v2, torch.zeros_like(q3), torch.zeros(B, 3, N), torch.zeros_like(q3))
