@@ -224,11 +224,13 @@ def fp8_table(steps=10, warmup=2):
             "hbm_peak_GBs": PEAK_HBM_GBS, "fp8_peak_tflops": PEAK_FP8_TFLOPS}
 
 
-def sweep():
-    """TFLOP/s of fa_fwd, fa_bwd and fa_fwd_fp8 over the metric's range of sequence lengths and head dims.
+def sweep(compact=False):
+    """TFLOP/s of the training forward (fa_fwd_ex with o_lo) and backward (fa_bwd_ex), and of
+    the FP8 forward, over the metric's range of sequence lengths and head dims.
 
     H = 16 and B = max(1, 32768 / N) heads of iid N(0, 1) bf16 activations drawn on
-    the device from a seeded generator (only timed, never checked here).
+    the device from a seeded generator (only timed, never checked here).  compact: fewer
+    launches per point and no FP8 forward (the form printed with the headline).
     """
     import torch
 
@@ -244,29 +246,59 @@ def sweep():
                 shape = (B, H, N, d)
                 q, k, v, do = (torch.randn(shape, generator=gen, device="cuda:0", dtype=torch.float32)
                                .to(torch.bfloat16) for _ in range(4))
-                o, lse = api.forward(q, k, v, None, causal)
+                o, lse, o_lo = api.forward_train(q, k, v, None, causal)
                 ws = torch.empty(api.bwd_workspace_size(B, H, N, d), dtype=torch.uint8, device="cuda:0")
-                n_it = max(3, min(20, int(2e12 / (4.0 * B * H * N * N * d))))
-                f_ms = time_calls(lambda: api.forward(q, k, v, None, causal, out=o, lse_out=lse), n_it)
-                b_ms = time_calls(lambda: api.backward(q, k, v, o, lse, do, None, causal, workspace=ws), n_it)
-                # FP8 forward on the same inputs (Q, K rotated), quantisation outside the timing
-                signs = torch.where(torch.rand(d, generator=gen, device="cuda:0") < 0.5, -1, 1).to(torch.int8)
-                q8, k8, v8 = api.quantize_fp8(q, signs), api.quantize_fp8(k, signs), api.quantize_fp8(v)
-                f8_ms = time_calls(lambda: api.forward_fp8(*q8, *k8, *v8, None, causal), n_it)
                 fl = 4.0 * B * H * N * N * d * (0.5 if causal else 1.0)
-                rows.append({"N": N, "d": d, "causal": causal, "B": B, "H": H,
-                             "fwd_ms": round(f_ms, 4), "fwd_tflops": round(fl / f_ms / 1e9, 1),
-                             "fwd_frac_peak": round(fl / f_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                             "bwd_ms": round(b_ms, 4), "bwd_tflops": round(2.5 * fl / b_ms / 1e9, 1),
-                             "bwd_frac_peak": round(2.5 * fl / b_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-                             "fwd_fp8_ms": round(f8_ms, 4), "fwd_fp8_tflops": round(fl / f8_ms / 1e9, 1),
-                             "fwd_fp8_frac_fp8_peak": round(fl / f8_ms / 1e9 / PEAK_FP8_TFLOPS, 4)})
-                print(f"sweep N={N} d={d} causal={causal}: fwd {rows[-1]['fwd_tflops']} TFLOP/s, "
-                      f"bwd {rows[-1]['bwd_tflops']} TFLOP/s, fwd fp8 {rows[-1]['fwd_fp8_tflops']} TFLOP/s",
+                n_it = max(2, min(10, int(1e12 / fl))) if compact else max(3, min(20, int(2e12 / fl)))
+                f_ms = time_calls(lambda: api.forward_train(q, k, v, None, causal, out=o, lse_out=lse,
+                                                            o_lo_out=o_lo), n_it)
+                b_ms = time_calls(lambda: api.backward(q, k, v, o, lse, do, None, causal, workspace=ws, o_lo=o_lo),
+                                  n_it)
+                row = {"N": N, "d": d, "causal": causal, "B": B, "H": H,
+                       "fwd_ms": round(f_ms, 4), "fwd_tflops": round(fl / f_ms / 1e9, 1),
+                       "fwd_frac_peak": round(fl / f_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                       "bwd_ms": round(b_ms, 4), "bwd_tflops": round(2.5 * fl / b_ms / 1e9, 1),
+                       "bwd_frac_peak": round(2.5 * fl / b_ms / 1e9 / PEAK_BF16_TFLOPS, 4)}
+                if not compact:
+                    # FP8 forward on the same inputs (Q, K rotated), quantisation outside the timing
+                    signs = torch.where(torch.rand(d, generator=gen, device="cuda:0") < 0.5, -1, 1).to(torch.int8)
+                    q8, k8, v8 = api.quantize_fp8(q, signs), api.quantize_fp8(k, signs), api.quantize_fp8(v)
+                    f8_ms = time_calls(lambda: api.forward_fp8(*q8, *k8, *v8, None, causal), n_it)
+                    row.update(fwd_fp8_ms=round(f8_ms, 4), fwd_fp8_tflops=round(fl / f8_ms / 1e9, 1),
+                               fwd_fp8_frac_fp8_peak=round(fl / f8_ms / 1e9 / PEAK_FP8_TFLOPS, 4))
+                    del q8, k8, v8
+                rows.append(row)
+                print(f"sweep N={N} d={d} causal={causal}: fwd {row['fwd_tflops']} TFLOP/s, "
+                      f"bwd {row['bwd_tflops']} TFLOP/s"
+                      + ("" if compact else f", fwd fp8 {row['fwd_fp8_tflops']} TFLOP/s"),
                       file=sys.stderr, flush=True)
-                del q, k, v, do, o, lse, ws, q8, k8, v8
+                del q, k, v, do, o, lse, o_lo, ws
                 torch.cuda.empty_cache()
     return rows
+
+
+def host_cpu():
+    """Model name, physical and logical core counts, and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        import psutil
+
+        physical = psutil.cpu_count(logical=False)
+    except Exception:  # pragma: no cover
+        physical = None
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        allowed = None
+    return {"model": model, "physical_cores": physical, "logical_cpus": os.cpu_count(), "allowed_cpus": allowed}
 
 
 def cpu_baseline(w, min_seconds=10.0, max_heads=4):
@@ -297,7 +329,8 @@ def cpu_baseline(w, min_seconds=10.0, max_heads=4):
     one_head = flops_fwd(w) / (w.B * w.H) * 3.5
     return {"value": heads * one_head / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"forward + backward of heads (0,0)..(0,{heads - 1}) of {w.name} [N={w.N}, d={w.d}, "
-                      f"causal] in fp64 NumPy, {dt:.1f} s; algorithmic flops of those heads"}
+                      f"causal] in fp64 NumPy, {dt:.1f} s; algorithmic flops of those heads",
+            "cores_meaning": "BLAS threads the oracle ran with", "cpu": host_cpu()}
 
 
 COPY_BYTES = 512 << 20
@@ -453,9 +486,16 @@ def main():
     f_fwd = flops_fwd(w)
     f_bwd = 2.5 * f_fwd
     f_step = (f_fwd if do_fwd else 0.0) + (f_bwd if do_bwd else 0.0)
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events])) if do_fwd else None
-    bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events])) if do_bwd else None
+    fwd_all = [e[0].elapsed_time(e[1]) for e in events] if do_fwd else None
+    bwd_all = [e[2].elapsed_time(e[3]) for e in events] if do_bwd else None
+    step_all = [e[0 if do_fwd else 2].elapsed_time(e[3 if do_bwd else 1]) for e in events]
+    fwd_ms = float(np.mean(fwd_all)) if do_fwd else None
+    bwd_ms = float(np.mean(bwd_all)) if do_bwd else None
     value = f_step * args.steps / elapsed / 1e12
+
+    def spread(ts):
+        return None if ts is None else {"mean": round(float(np.mean(ts)), 4), "median": round(float(np.median(ts)), 4),
+                                        "min": round(float(np.min(ts)), 4), "max": round(float(np.max(ts)), 4)}
 
     # dominant launch by time: fa_bwd (its kernels bwd_prep, bwd_dkdv and bwd_dq run
     # back to back on the stream and are timed together, as one launch of the
@@ -493,10 +533,15 @@ def main():
         "bwd": None if bwd_ms is None else {"ms": round(bwd_ms, 4), "tflops": round(f_bwd / bwd_ms / 1e9, 2),
                                             "frac_peak": round(f_bwd / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
         "roofline": roofline,
+        # per-step spread (HIP events around each launch); the step is forward + backward
+        "ms_spread": {"step": spread(step_all), "fwd": spread(fwd_all), "bwd": spread(bwd_all),
+                      "step_tflops_at_median": round(f_step / float(np.median(step_all)) / 1e9, 2)},
     }
     if not args.no_extra and args.only == "step":
-        del tq, tk, tv, tdo, o, lse, ws
+        del tq, tk, tv, tdo, o, lse, o_lo, ws
         torch.cuda.empty_cache()
+        # the metric's range: training forward and backward over N = 512..64K, d = 64/128, causal 0/1
+        out["sweep"] = sweep(compact=True)
         out["workloads"] = kernel_table()
         out["fp8"] = fp8_table()
         g = gemm_reference()
