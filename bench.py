@@ -381,12 +381,43 @@ def measured_traffic(which):
 
 
 def profile_summary(d):
-    """Text summary of a rocprofv3 output tree: kernel-trace stats and PMC byte counters."""
+    """Text summary of a rocprofv3 output tree (CSV files, or the SQLite results database):
+    kernel-trace stats and PMC counters per dispatch."""
     import csv
     import glob
+    import sqlite3
     from collections import defaultdict
 
     lines = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*results.db"), recursive=True)):
+        con = sqlite3.connect(f)
+        rows = con.execute("select name, duration from kernels").fetchall()
+        if rows:
+            per = defaultdict(list)
+            for name, dur in rows:
+                per[name].append(dur / 1e3)
+            total = sum(sum(v) for v in per.values())
+            lines.append(f"kernel-trace stats ({os.path.relpath(f, d)}):")
+            lines.append(f"  {'calls':>5} {'avg us':>10} {'median us':>10} {'min us':>10} {'max us':>10} {'%':>6}  kernel")
+            for name, v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+                sv = sorted(v)
+                lines.append(f"  {len(v):>5} {sum(v) / len(v):10.1f} {sv[len(sv) // 2]:10.1f} {sv[0]:10.1f} "
+                             f"{sv[-1]:10.1f} {100.0 * sum(v) / total:6.2f}  {name[:90]}")
+        crow = con.execute("select dispatch_id, kernel_name, counter_name, value from counters_collection").fetchall()
+        if crow:
+            disp = defaultdict(float)
+            names = {}
+            for did, kname, cname, val in crow:
+                disp[(did, cname)] += val
+                names[did] = kname
+            agg = defaultdict(list)
+            for (did, cname), val in disp.items():
+                agg[(cname, names[did])].append(val)
+            lines.append(f"pmc ({os.path.relpath(f, d)}):")
+            for (c, k), v in agg.items():
+                unit = " KiB" if c in ("FETCH_SIZE", "WRITE_SIZE") else ""
+                lines.append(f"  {c:>10} {len(v):3d} dispatches, mean {sum(v) / len(v):16.1f}{unit}  {k[:90]}")
+        con.close()
     for f in sorted(glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)):
         lines.append(f"kernel-trace stats ({os.path.relpath(f, d)}):")
         lines.append(f"  {'calls':>5} {'avg us':>10} {'min us':>10} {'max us':>10} {'%':>6}  kernel")
