@@ -9,6 +9,8 @@ h // (H // H_kv), and the dense entry points route to fa_fwd_gqa / fa_bwd_gqa.
 
 from __future__ import annotations
 
+import contextlib
+import functools
 from typing import Optional, Tuple
 
 import torch
@@ -76,9 +78,17 @@ def _outputs(q: torch.Tensor, out, lse_out, with_lse: bool):
     return o, lse
 
 
+@functools.lru_cache(maxsize=None)
 def default_scale(d: int) -> float:
     """1/sqrt(d) as the fp32 value the kernels receive."""
     return float(torch.tensor(1.0, dtype=torch.float32) / torch.tensor(float(d), dtype=torch.float32).sqrt())
+
+
+def _on_device(device: torch.device):
+    """Make `device` current for the library call (a no-op when it already is)."""
+    if device.index is None or torch.cuda.current_device() == device.index:
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
 
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
@@ -95,7 +105,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[f
     o, lse = _outputs(q, out, lse_out, with_lse)
     lib = _lib.load()
     lse_ptr = lse.data_ptr() if lse is not None else None
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         if hkv == H:
             st = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse_ptr, B, H, N, d, scale,
                             int(bool(causal)), _DTYPES[q.dtype], _stream_ptr(q.device))
@@ -123,7 +133,7 @@ def forward_blocksparse(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), block_mask.data_ptr(), o.data_ptr(),
             lse.data_ptr() if lse is not None else None)
     tail = (N, d, scale, int(bool(causal)), _DTYPES[q.dtype], _stream_ptr(q.device))
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         if hkv == H:
             st = lib.fa_fwd_blocksparse(*ptrs, B, H, *tail)
         else:
@@ -159,7 +169,7 @@ def forward_train(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Opti
     elif o_lo_out is not None:
         raise ValueError("o_lo_out applies to bfloat16 inputs only")
     lib = _lib.load()
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         st = lib.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                            None if block_mask is None else block_mask.data_ptr(), o.data_ptr(),
                            None if o_lo is None else o_lo.data_ptr(), lse.data_ptr(), B, H, hkv, N, d, scale,
@@ -227,7 +237,7 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             workspace.numel() * workspace.element_size(), _stream_ptr(q.device))
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         if o_lo is not None:
             name = "fa_bwd_ex"
             st = lib.fa_bwd_ex(*ptrs[:3], None if block_mask is None else block_mask.data_ptr(), ptrs[3],
@@ -275,7 +285,7 @@ def backward_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
     _check_buffer(dv, k.shape, grad_dtype, q.device, "dv")
     scale = default_scale(d) if scale is None else float(scale)
     lib = _lib.load()
-    with torch.cuda.device(q.device):
+    with _on_device(q.device):
         st = lib.fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                 None if block_mask is None else block_mask.data_ptr(), o.data_ptr(),
                                 None if o_lo is None else o_lo.data_ptr(), lse.data_ptr(), do.data_ptr(),
@@ -335,7 +345,7 @@ def quantize_fp8(x: torch.Tensor, signs: Optional[torch.Tensor] = None) -> Tuple
         signs = signs.contiguous()
     codes = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
     scales = torch.empty(fp8_scale_shape(B, H, N), dtype=torch.float32, device=x.device)
-    with torch.cuda.device(x.device):
+    with _on_device(x.device):
         st = _lib.load().fa_quantize_fp8(x.data_ptr(), None if signs is None else signs.data_ptr(),
                                          codes.data_ptr(), scales.data_ptr(), B, H, N, d, _DTYPES[x.dtype],
                                          _stream_ptr(x.device))
@@ -364,7 +374,7 @@ def forward_fp8(q8: torch.Tensor, q_scale: torch.Tensor, k8: torch.Tensor, k_sca
     scale = default_scale(d) if scale is None else float(scale)
     o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=q8.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q8.device) if with_lse else None
-    with torch.cuda.device(q8.device):
+    with _on_device(q8.device):
         st = _lib.load().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), q_scale.data_ptr(),
                                     k_scale.data_ptr(), v_scale.data_ptr(), o.data_ptr(),
                                     None if lse is None else lse.data_ptr(), B, H, hkv, N, d, scale,

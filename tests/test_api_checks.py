@@ -37,7 +37,7 @@ def fake_lib(monkeypatch):
     monkeypatch.setattr(_lib, "load", lambda: FakeLib())
     monkeypatch.setattr(api, "_on_gpu", lambda t: True)
     monkeypatch.setattr(api, "_stream_ptr", lambda device: 0)
-    monkeypatch.setattr(torch.cuda, "device", lambda device: _NullContext())
+    monkeypatch.setattr(api, "_on_device", lambda device: _NullContext())
 
 
 class _NullContext:
