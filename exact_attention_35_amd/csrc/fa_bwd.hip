@@ -422,10 +422,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
 //     and dS = P (dP - D), packed to bf16 and handed over through LDS;
 //   gradient wave (w >= 4): dV^T += dO^T P and dK^T += Q^T dS for the same keys,
 //     the dO^T / Q^T operands read from the tiles with transposing LDS reads.
-// Step i, phase a: the score waves hand over dS(i) and run the MFMAs of tile
+// Step i, phase a: the score waves hand over dS(i) and run the S MFMAs of tile
 // i+1 while the gradient waves run dV += dO(i)^T P(i); phase b: the score waves
-// compute P(i+1), dS(i+1) and hand over P(i+1) while the gradient waves fetch
-// tile i+2 and run dK += Q(i)^T dS(i).  Q and dO tiles (64 queries, K layout)
+// compute P(i+1) interleaved with the dP MFMAs of tile i+1 and hand over P(i+1)
+// while the gradient waves fetch tile i+2 and run dK += Q(i)^T dS(i).  Q and dO tiles (64 queries, K layout)
 // and their (lse log2 e, -D) rows sit in rings of three buffers.
 // ---------------------------------------------------------------------------
 // MFMA / LDS-read interleave of an MFMA phase (masks: 0x8 MFMA, 0x100 LDS read):
@@ -603,7 +603,7 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
     const KOffsets<D> ko = k_offsets<D>(l32, half);
     f32x16 s[NSB], dp[NSB];
     bf16x8 pf[NPT], dsf[NPT];
-    // S = K Q^T of one tile (from zero) and dP - D = V dO^T - D (from dp = -D, set by p_body)
+    // S = K Q^T of one tile (from zero)
     auto s_mfma = [&](const unsigned short* qb) __attribute__((always_inline)) {
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -612,52 +612,72 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
       sched_one_read_per_mfma<NSB * (D / 16)>();
       __builtin_amdgcn_s_setprio(0);
     };
-    auto dp_mfma = [&](const unsigned short* ob) __attribute__((always_inline)) {
-      __builtin_amdgcn_s_setprio(1);
-      qk_ring_tile<D, BQ>(ob, ko, vf, dp);
-      sched_one_read_per_mfma<NSB * (D / 16)>();
-      __builtin_amdgcn_s_setprio(0);
-    };
-    // P of tile i (register r of block b is query 32b + acc_row_swapped(r, half)), kept in s
-    // as fp32 for dS and packed for the handover; dp starts at -D of the same query, read
-    // from LDS straight into the accumulator.
-    // The masked variant is a separate copy so that the common path has no per-element selects.
-    auto p_body = [&](int q0, const float2* st, auto mask_tag) __attribute__((always_inline)) {
+    // P of tile i and dP(i) - D = V dO^T - D together, in one fixed instruction order: dp
+    // starts at -D (read from LDS straight into the accumulator), then each dP MFMA is
+    // followed by the LDS operand read of the MFMA AHEAD places later and by the
+    // exponentials of PER scores, with scheduling fences between the slices, so that
+    // the wave's vector work issues while its own MFMAs run.  P (register r of block b
+    // is query 32b + acc_row_swapped(r, half)) goes to s (fp32, for dS) and to pf (bf16,
+    // for the handover).  The masked variant is a separate copy so that the common path
+    // has no per-element selects.
+    auto p_dp_fused = [&](int q0, const float2* st, const unsigned short* ob, auto mask_tag)
+                          __attribute__((always_inline)) {
       constexpr bool MASKED = decltype(mask_tag)::value;
+      constexpr int NM = NSB * (D / 16);  // dP MFMAs: chunk m / NSB, block m % NSB
+      constexpr int NE = 16 * NSB;        // P elements per lane
+      constexpr int PER = NE / NM;
+      constexpr int AHEAD = 4;
+      static_assert(PER * NM == NE, "whole slices of P per MFMA");
+      f32x4 lq[NSB][4];
 #pragma unroll
       for (int b = 0; b < NSB; ++b) {
-        // registers 8g + e are queries 32b + 16g + 8h + e, e = 0..7: per g two four-row
-        // groups (lse log2 e x 4, then -D x 4); the four -D quads form dp[b] as one tuple
         const f32x4* src = reinterpret_cast<const f32x4*>(st + 32 * b + 8 * half);
         dp[b] = __builtin_shufflevector(__builtin_shufflevector(src[1], src[3], 0, 1, 2, 3, 4, 5, 6, 7),
                                         __builtin_shufflevector(src[9], src[11], 0, 1, 2, 3, 4, 5, 6, 7), 0, 1, 2,
                                         3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const f32x4 l0 = src[8 * g], l1 = src[8 * g + 2];
-          const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = 8 * g + e;
-            float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -lv[e]));
-            if (MASKED) {
-              // query = base + off with off = 16(r/8) + (r%8) a constant
-              const int base = q0 + 32 * b + 8 * half;
-              const int off = 16 * (r >> 3) + (r & 7);
-              const bool hide = off >= N - base || (CAUSAL && off < mykey - base);
-              p = hide ? 0.f : p;
-            }
-            s[b][r] = p;
-          }
-        }
+        lq[b][0] = src[0];
+        lq[b][1] = src[2];
+        lq[b][2] = src[8];
+        lq[b][3] = src[10];
       }
+      int o[D / 16];
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) o[cc] = fresh(ko.off[cc]);
+      bf16x8 ring[AHEAD];
+#pragma unroll
+      for (int m = 0; m < AHEAD; ++m) ring[m] = lds_bf16x8(ob + 32 * (m % NSB) * D + o[m / NSB]);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const bf16x8 x = ring[m % AHEAD];
+        if (m + AHEAD < NM) ring[m % AHEAD] = lds_bf16x8(ob + 32 * ((m + AHEAD) % NSB) * D + o[(m + AHEAD) / NSB]);
+        dp[m % NSB] = mfma32(x, vf[m / NSB], dp[m % NSB]);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int k = m * PER + e;
+          const int b = k >> 4, r = k & 15;
+          const float lv = lq[b][2 * (r >> 3) + ((r & 7) >> 2)][r & 3];
+          float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -lv));
+          if (MASKED) {
+            // query = base + off with off = 16(r/8) + (r%8) a constant
+            const int base = q0 + 32 * b + 8 * half;
+            const int off = 16 * (r >> 3) + (r & 7);
+            const bool hide = off >= N - base || (CAUSAL && off < mykey - base);
+            p = hide ? 0.f : p;
+          }
+          s[b][r] = p;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int t2 = 0; t2 < NPT; ++t2) pf[t2] = pack_bf16(s[t2 >> 1], 8 * (t2 & 1));
     };
-    auto p_vector = [&](int i, const float2* st) __attribute__((always_inline)) {
+    auto p_dp = [&](int i, const float2* st, const unsigned short* ob) __attribute__((always_inline)) {
       const int q0 = i < T ? tile_q(i) * BQ : N;  // past the last tile: everything masked
-      if ((q0 + BQ > N) || (CAUSAL && q0 < wave_k0 + 31)) p_body(q0, st, std::true_type{});
-      else p_body(q0, st, std::false_type{});
+      if ((q0 + BQ > N) || (CAUSAL && q0 < wave_k0 + 31)) p_dp_fused(q0, st, ob, std::true_type{});
+      else p_dp_fused(q0, st, ob, std::false_type{});
     };
     // dS = P (dP - D); a masked P is 0, and so is its dS (dP - D is finite)
     auto ds_vector = [&]() __attribute__((always_inline)) {
@@ -681,17 +701,15 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
       for (int t2 = 0; t2 < NPT; ++t2) xch[sw][NPT + t2][lane] = as_uint4(dsf[t2]);
       s_mfma(qnxt);
       barrier_ring<15>();  // the dS handover writes have completed
-      p_vector(i + 1, snxt);
+      p_dp(i + 1, snxt, onxt);
 #pragma unroll
       for (int t2 = 0; t2 < NPT; ++t2) xch[sw][t2][lane] = as_uint4(pf[t2]);
-      dp_mfma(onxt);
       barrier_ring<15>();  // the P handover writes have completed
     };
     s_mfma(qbuf_0);
-    p_vector(0, st_0);
+    p_dp(0, st_0, obuf_0);
 #pragma unroll
     for (int t2 = 0; t2 < NPT; ++t2) xch[sw][t2][lane] = as_uint4(pf[t2]);
-    dp_mfma(obuf_0);
     barrier_ring<15>();
     for (int i = 0; i < T; i += 3) {
       step(i, qbuf_1, obuf_1, st_1);

@@ -180,14 +180,15 @@ def test_blocksparse_grouped_query_equals_repeated_kv(d):
 
 def test_autograd_wrapper_grouped_query():
     """api.attention with 8 query heads on 2 K/V heads: output and gradients (dK, dV of the
-    shared heads' shape) equal the explicit fa_fwd_gqa / fa_bwd_gqa calls bit for bit."""
+    shared heads' shape) equal the explicit fa_fwd_ex / fa_bwd_ex calls (with o_lo) bit for bit."""
     announce("autograd wrapper, grouped-query")
     q, k, v, do = inputs.random_case(30, 1, 8, 200, 64, "bf16", backward=True, h_kv=2)
     tq, tk, tv = (dev(x, BF).requires_grad_(True) for x in (q, k, v))
     out = api.attention(tq, tk, tv, None, True)
     out.backward(dev(do, BF))
-    o, lse = api.forward(tq.detach(), tk.detach(), tv.detach(), None, True)
-    eq = api.backward(tq.detach(), tk.detach(), tv.detach(), o, lse, dev(do, BF), None, True, grad_dtype=BF)
+    o, lse, o_lo = api.forward_train(tq.detach(), tk.detach(), tv.detach(), None, True)
+    eq = api.backward(tq.detach(), tk.detach(), tv.detach(), o, lse, dev(do, BF), None, True, grad_dtype=BF,
+                      o_lo=o_lo)
     torch.cuda.synchronize()
     assert torch.equal(out.detach(), o)
     assert tk.grad.shape == tk.shape and tv.grad.shape == tv.shape
@@ -197,7 +198,7 @@ def test_autograd_wrapper_grouped_query():
 
 def test_autograd_wrapper_grouped_query_with_block_mask():
     """api.attention with 8 query heads on 2 K/V heads and a block mask: output and gradients
-    equal the explicit fa_fwd_blocksparse_gqa / fa_bwd_blocksparse_gqa calls bit for bit."""
+    equal the explicit fa_fwd_ex / fa_bwd_ex calls (mask and o_lo) bit for bit."""
     announce("autograd wrapper, grouped-query, block-sparse")
     n = 400
     q, k, v, do = inputs.random_case(36, 1, 8, n, 64, "bf16", backward=True, h_kv=2)
@@ -206,9 +207,9 @@ def test_autograd_wrapper_grouped_query_with_block_mask():
     tq, tk, tv = (dev(x, BF).requires_grad_(True) for x in (q, k, v))
     out = api.attention(tq, tk, tv, None, True, tm)
     out.backward(dev(do, BF))
-    o, lse = api.forward_blocksparse(tq.detach(), tk.detach(), tv.detach(), tm, None, True)
+    o, lse, o_lo = api.forward_train(tq.detach(), tk.detach(), tv.detach(), None, True, block_mask=tm)
     eq = api.backward(tq.detach(), tk.detach(), tv.detach(), o, lse, dev(do, BF), None, True, grad_dtype=BF,
-                      block_mask=tm)
+                      o_lo=o_lo, block_mask=tm)
     torch.cuda.synchronize()
     assert torch.equal(out.detach(), o)
     assert tk.grad.shape == tk.shape and tv.grad.shape == tv.shape

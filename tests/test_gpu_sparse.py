@@ -149,7 +149,7 @@ def test_blocksparse_backward_many_windows_bf16_gradients():
 
 def test_autograd_wrapper_with_block_mask():
     """api.attention with a block mask: the forward and the gradients equal the explicit
-    fa_fwd_blocksparse / fa_bwd_blocksparse calls (bf16 gradients), and the oracle."""
+    fa_fwd_ex / fa_bwd_ex calls with the mask and o_lo (bf16 gradients), and the oracle."""
     n, d = 300, 64
     nb = -(-n // 128)
     announce("autograd wrapper, block-sparse")
@@ -159,9 +159,9 @@ def test_autograd_wrapper_with_block_mask():
     tq, tk, tv = (dev(x, BF).requires_grad_(True) for x in (q, k, v))
     out = api.attention(tq, tk, tv, None, True, tm)
     out.backward(dev(do, BF))
-    o, lse = api.forward_blocksparse(tq.detach(), tk.detach(), tv.detach(), tm, None, True)
+    o, lse, o_lo = api.forward_train(tq.detach(), tk.detach(), tv.detach(), None, True, block_mask=tm)
     eq = api.backward(tq.detach(), tk.detach(), tv.detach(), o, lse, dev(do, BF), None, True, grad_dtype=BF,
-                      block_mask=tm)
+                      block_mask=tm, o_lo=o_lo)
     torch.cuda.synchronize()
     assert torch.equal(out.detach(), o)
     for g, e in zip((tq.grad, tk.grad, tv.grad), eq):
