@@ -344,14 +344,14 @@ COPY_BYTES = 512 << 20
 TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
-    # fwd_bf16_kernel
-    "fwd": {"fetch_kib": 241201.0, "write_kib": 66561.3,
+    # fwd_bf16_kernel writing o, o_lo and lse (fa_fwd_ex)
+    "fwd": {"fetch_kib": 256120.6, "write_kib": 133294.5,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "ce10357b2478a6bf8739845889e411e5778bc26311878750502524b3f0881268"},
-    # bwd_prep_kernel + bwd_dkdv_kernel + bwd_dq_kernel
-    "bwd": {"fetch_kib": 66575.4 + 366484.7 + 319621.4, "write_kib": 2048.0 + 262144.0 + 131072.0,
+            "sha256": "1ccd677341c99754bf7f9e716d4edf4f5b6cc487421a52eacd58eab5dbd438f6"},
+    # bwd_prep_kernel (reading o, o_lo, dO) + bwd_dkdv_kernel + bwd_dq_kernel (fa_bwd_ex)
+    "bwd": {"fetch_kib": 99346.6 + 363160.1 + 321877.0, "write_kib": 2049.8 + 262144.0 + 131072.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "5694f7125a291010990f447f0e80002591ffc4ddb6dafb8c98d561bb37774d48"},
+            "sha256": "31c39024adbaf48e39c455f60080b412775ded8a418ae5a51ad25c7046d9b99f"},
 }
 
 
@@ -473,7 +473,7 @@ def main():
         print(json.dumps({"fp8": fp8_table(args.steps, args.warmup)}), flush=True)
         return
     w = inputs.WORKLOADS[args.workload]
-    assert w.dtype == "bf16" and not w.sparse, "the step times a dense bf16 workload"
+    assert w.dtype == "bf16", "the step times a bf16 workload"
     q, k, v, _ = inputs.make_qkv(w)
     do = inputs.draw(w.index, inputs.SLOT_DO, w.shape)
     bf = torch.bfloat16
@@ -482,24 +482,30 @@ def main():
     o = torch.empty_like(tq)
     o_lo = torch.empty_like(tq)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda:0")
-    ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d, H_kv=w.kv_heads), dtype=torch.uint8,
+                     device="cuda:0")
+    density, tm = None, None
+    if w.sparse:  # the block-sparse workload: its tile mask, and flops scaled by its density
+        mask = inputs.make_block_mask(-(-w.N // inputs.MASK_BLOCK), w.density, w.index, causal=w.causal)
+        density = sparse_density(mask)
+        tm = torch.from_numpy(mask).to("cuda:0")
 
     do_fwd = args.only in ("step", "fwd")
     do_bwd = args.only in ("step", "bwd")
     if not do_fwd:
-        api.forward_train(tq, tk, tv, w.scale, w.causal, out=o, lse_out=lse, o_lo_out=o_lo)
+        api.forward_train(tq, tk, tv, w.scale, w.causal, block_mask=tm, out=o, lse_out=lse, o_lo_out=o_lo)
 
     def step(ev=None):
         if do_fwd:
             if ev is not None:
                 ev[0].record()
-            api.forward_train(tq, tk, tv, w.scale, w.causal, out=o, lse_out=lse, o_lo_out=o_lo)
+            api.forward_train(tq, tk, tv, w.scale, w.causal, block_mask=tm, out=o, lse_out=lse, o_lo_out=o_lo)
             if ev is not None:
                 ev[1].record()
         if do_bwd:
             if ev is not None:
                 ev[2].record()
-            api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws, o_lo=o_lo)
+            api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws, block_mask=tm, o_lo=o_lo)
             if ev is not None:
                 ev[3].record()
 
@@ -514,7 +520,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    f_fwd = flops_fwd(w)
+    f_fwd = flops_fwd(w, density)
     f_bwd = 2.5 * f_fwd
     f_step = (f_fwd if do_fwd else 0.0) + (f_bwd if do_bwd else 0.0)
     fwd_all = [e[0].elapsed_time(e[1]) for e in events] if do_fwd else None
@@ -556,6 +562,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "kv_heads": w.kv_heads, "block_sparse_density": density,
                    "step": {"step": "fa_fwd_ex + fa_bwd_ex (with o_lo)", "fwd": "fa_fwd_ex",
                             "bwd": "fa_bwd_ex"}[args.only],
                    "parallelism": "none (one GPU)"},
@@ -569,7 +576,7 @@ def main():
                       "step_tflops_at_median": round(f_step / float(np.median(step_all)) / 1e9, 2)},
     }
     if not args.no_extra and args.only == "step":
-        del tq, tk, tv, tdo, o, lse, o_lo, ws
+        del tq, tk, tv, tdo, o, lse, o_lo, ws, tm
         torch.cuda.empty_cache()
         # the metric's range: training forward and backward over N = 512..64K, d = 64/128, causal 0/1
         out["sweep"] = sweep(compact=True)
