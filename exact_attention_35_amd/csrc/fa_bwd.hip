@@ -9,13 +9,16 @@
 //   dV  = P^T dO    dP = dO V^T    dS = P * (dP - D)
 //   dQ  = scale dS K              dK = scale dS^T Q
 //
-// bf16 path, three kernels:
-//   * bwd_prep_kernel: per row, D and lse log2(e) (+inf for a row with no
-//     visible key, so that its P is 0), stored as one float2;
+// bf16 path, two kernels, in this order:
+//   * bwd_dq_kernel: one workgroup owns 256 queries; each lane already holds
+//     its query's dO row, so it first forms D and lse log2(e) (+inf for a row
+//     with no visible key, so that its P is 0) and stores them as one float2
+//     per row; it then streams K and V tiles through LDS and accumulates dQ in
+//     registers;
 //   * bwd_dkdv_kernel: one workgroup owns 128 keys; it streams 64-query tiles
-//     of Q and dO through LDS and accumulates dK, dV in registers;
-//   * bwd_dq_kernel: one workgroup owns 256 queries; it streams K and V tiles
-//     through LDS and accumulates dQ in registers.
+//     of Q and dO (and the stored row pairs) through LDS and accumulates dK,
+//     dV in registers.
+// The fp32 path forms the row pairs in a kernel of their own (bwd_prep_kernel).
 // Each gradient is owned by exactly one workgroup, so there are no atomics
 // and the results are deterministic; the price is that S and dP are
 // recomputed by both the dK/dV and the dQ kernel (seven tile contractions per
@@ -33,44 +36,22 @@
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// stats[row] = (lse * log2 e, -D) with D = rowsum(dO * O).  T = unsigned short (bf16 bits) or float.
-// With olo (bf16 only), O is taken as o + olo, the stored output plus its low-order part.
+// fp32 path: stats[row] = (lse * log2 e, -D) with D = rowsum(dO * O).
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, const T* __restrict__ olo,
-                                                       const T* __restrict__ dO, const float* __restrict__ lse,
-                                                       float2* __restrict__ stats, long long rows) {
-  constexpr int EPT = 16 / sizeof(T);  // elements per 16-byte load
-  constexpr int TPR = D / EPT;         // threads per row
-  constexpr int RPB = 256 / TPR;       // rows per block
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ o, const float* __restrict__ dO,
+                                                       const float* __restrict__ lse, float2* __restrict__ stats,
+                                                       long long rows) {
+  constexpr int TPR = D / 4;     // threads per row, 4 floats each
+  constexpr int RPB = 256 / TPR;  // rows per block
   const int tid = threadIdx.x;
   const long long row = (long long)blockIdx.x * RPB + tid / TPR;
   const int part = tid % TPR;
   float acc = 0.f;
   if (row < rows) {
-    const uint4 ov = *reinterpret_cast<const uint4*>(o + row * D + part * EPT);
-    const uint4 dv = *reinterpret_cast<const uint4*>(dO + row * D + part * EPT);
-    if (sizeof(T) == 2) {
-      const unsigned short* a = reinterpret_cast<const unsigned short*>(&ov);
-      const unsigned short* b = reinterpret_cast<const unsigned short*>(&dv);
-      if (olo != nullptr) {
-        const uint4 lv = *reinterpret_cast<const uint4*>(olo + row * D + part * EPT);
-        const unsigned short* c = reinterpret_cast<const unsigned short*>(&lv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float g = bf16_bits_to_float(b[e]);
-          acc = fmaf(bf16_bits_to_float(a[e]), g, fmaf(bf16_bits_to_float(c[e]), g, acc));
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(bf16_bits_to_float(a[e]), bf16_bits_to_float(b[e]), acc);
-      }
-    } else {
-      const float* a = reinterpret_cast<const float*>(&ov);
-      const float* b = reinterpret_cast<const float*>(&dv);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = fmaf(a[e], b[e], acc);
-    }
+    const float4 ov = *reinterpret_cast<const float4*>(o + row * D + part * 4);
+    const float4 gv = *reinterpret_cast<const float4*>(dO + row * D + part * 4);
+    acc = fmaf(ov.w, gv.w, fmaf(ov.z, gv.z, fmaf(ov.y, gv.y, ov.x * gv.x)));
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
@@ -129,7 +110,10 @@ struct BwdBf16Args {
   const unsigned short* k;
   const unsigned short* v;
   const unsigned short* dO;
-  const float2* stats;  // per row: (lse log2 e, -D)
+  const unsigned short* o;    // the forward's output, for D (dQ kernel)
+  const unsigned short* olo;  // its low-order part, or null
+  const float* lse;           // the forward's row log-sum-exp (dQ kernel)
+  float2* stats;  // per row: (lse log2 e, -D), written by the dQ kernel for the dK/dV kernel
   const unsigned char* mask;  // block-sparse 128x128 tile mask [nb, nb], or null
   int nb;
   void* dq;
@@ -320,11 +304,34 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
       dof[c] = as_bf16x8(buf_load16(dores, off));
     }
   }
-  float lse2 = INFINITY, dlt = 0.f;  // rows past N: P = 0
+  // D = rowsum(dO * O) of this lane's query (O taken as o + o_lo when the low-order part is
+  // given; each half-wave sums its half of the row) and lse log2 e; the pair is also stored
+  // for the dK/dV kernel, which runs next.  Rows past N: P = 0.
+  float dpart = 0.f;
+  {
+    const BufRes ores = make_buf(a.o + hoff, head_bytes);
+    const bool with_lo = a.olo != nullptr;
+    const BufRes lres = make_buf(with_lo ? a.olo + hoff : a.o + hoff, head_bytes);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const unsigned int off = (unsigned int)(qrow * D + 16 * c + 8 * half) * 2;  // rows past N: zeros
+      const uint4 ov = buf_load16(ores, off);
+      const uint4 lv = with_lo ? buf_load16(lres, off) : zero_uint4();
+      const uint4 gv = as_uint4(dof[c]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float g = bf16_bits_to_float(bf16_lane_of(gv, e));
+        dpart = fmaf(bf16_bits_to_float(bf16_lane_of(ov, e)), g,
+                     fmaf(bf16_bits_to_float(bf16_lane_of(lv, e)), g, dpart));
+      }
+    }
+  }
+  const float dlt = xhalf_sum(dpart);
+  float lse2 = INFINITY;
   if (qrow < N) {
-    const float2 st = a.stats[(size_t)bh * N + qrow];
-    lse2 = st.x;
-    dlt = -st.y;
+    const float l = a.lse[(size_t)bh * N + qrow];
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;  // +inf: a row with no visible key has P = 0
+    if (half == 0) a.stats[(size_t)bh * N + qrow] = make_float2(lse2, -dlt);
   }
   const KOffsets<D> ko = k_offsets<D>(l32, half);
   const KtOffsets<D> kto = kt_offsets<D>(lane);
@@ -959,15 +966,13 @@ static void launch_group_sum(const BwdParams& p, hipStream_t stream) {
                        p.dv, quads, head_quads, p.H / p.Hkv);
 }
 
-template <typename T, int D>
-static void launch_prep(const BwdParams& p, hipStream_t stream) {
-  constexpr int EPT = 16 / sizeof(T);
-  constexpr int RPB = 256 / (D / EPT);
+template <int D>
+static void launch_prep_f32(const BwdParams& p, hipStream_t stream) {
+  constexpr int RPB = 256 / (D / 4);
   const long long rows = (long long)p.B * p.H * p.N;
   const unsigned blocks = (unsigned)((rows + RPB - 1) / RPB);
-  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3(blocks), dim3(256), 0, stream, static_cast<const T*>(p.o),
-                     static_cast<const T*>(p.o_lo), static_cast<const T*>(p.dO), p.lse,
-                     reinterpret_cast<float2*>(p.stats), rows);
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(blocks), dim3(256), 0, stream, static_cast<const float*>(p.o),
+                     static_cast<const float*>(p.dO), p.lse, reinterpret_cast<float2*>(p.stats), rows);
 }
 
 template <int D, bool CAUSAL, bool SPARSE>
@@ -977,7 +982,10 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   a.k = static_cast<const unsigned short*>(p.k);
   a.v = static_cast<const unsigned short*>(p.v);
   a.dO = static_cast<const unsigned short*>(p.dO);
-  a.stats = reinterpret_cast<const float2*>(p.stats);
+  a.o = static_cast<const unsigned short*>(p.o);
+  a.olo = static_cast<const unsigned short*>(p.o_lo);
+  a.lse = p.lse;
+  a.stats = reinterpret_cast<float2*>(p.stats);
   a.dq = p.dq;
   a.dk = p.dk;
   a.dv = p.dv;
@@ -1007,11 +1015,12 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
     akv.dv = p.part_v;
     akv.grad_bf16 = 0;
   }
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(nkb * (unsigned)a.BH), dim3(512), dyn_kv, stream,
-                     akv);
+  // the dQ kernel first: it also forms D and stores each row's (lse log2 e, -D) for the dK/dV kernel
   const unsigned nqb = (unsigned)((p.N + 255) / 256);
   hipLaunchKernelGGL((bwd_dq_kernel<D, DQ_BN, CAUSAL, SPARSE>), dim3(nqb * (unsigned)a.BH), dim3(512), dyn_q, stream,
                      a);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(nkb * (unsigned)a.BH), dim3(512), dyn_kv, stream,
+                     akv);
 }
 
 template <int D, bool CAUSAL>
@@ -1040,10 +1049,10 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   (void)hipGetLastError();  // clear an error left by an earlier, unrelated HIP call
   if (p.dtype == 0) {
     if (p.d == 64) {
-      launch_prep<float, 64>(p, stream);
+      launch_prep_f32<64>(p, stream);
       if (p.causal) launch_bwd_f32<64, true>(p, stream); else launch_bwd_f32<64, false>(p, stream);
     } else {
-      launch_prep<float, 128>(p, stream);
+      launch_prep_f32<128>(p, stream);
       if (p.causal) launch_bwd_f32<128, true>(p, stream); else launch_bwd_f32<128, false>(p, stream);
     }
     if (p.Hkv < p.H) launch_group_sum(p, stream);
@@ -1051,14 +1060,12 @@ hipError_t launch_bwd(const BwdParams& p, hipStream_t stream) {
   }
   const bool sparse = p.mask != nullptr;
   if (p.d == 64) {
-    launch_prep<unsigned short, 64>(p, stream);
     if (sparse) {
       if (p.causal) launch_bwd_bf16<64, true, true>(p, stream); else launch_bwd_bf16<64, false, true>(p, stream);
     } else {
       if (p.causal) launch_bwd_bf16<64, true, false>(p, stream); else launch_bwd_bf16<64, false, false>(p, stream);
     }
   } else {
-    launch_prep<unsigned short, 128>(p, stream);
     if (sparse) {
       if (p.causal) launch_bwd_bf16<128, true, true>(p, stream); else launch_bwd_bf16<128, false, true>(p, stream);
     } else {
