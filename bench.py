@@ -348,10 +348,10 @@ MEASURED_TRAFFIC = {
     "fwd": {"fetch_kib": 256120.6, "write_kib": 133294.5,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
             "sha256": "1ccd677341c99754bf7f9e716d4edf4f5b6cc487421a52eacd58eab5dbd438f6"},
-    # bwd_prep_kernel (reading o, o_lo, dO) + bwd_dkdv_kernel + bwd_dq_kernel (fa_bwd_ex)
-    "bwd": {"fetch_kib": 99346.6 + 363160.1 + 321877.0, "write_kib": 2049.8 + 262144.0 + 131072.0,
+    # bwd_dq_kernel (also reading o, o_lo for D) + bwd_dkdv_kernel (fa_bwd_ex)
+    "bwd": {"fetch_kib": 384759.2 + 362549.4, "write_kib": 133120.0 + 262144.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "31c39024adbaf48e39c455f60080b412775ded8a418ae5a51ad25c7046d9b99f"},
+            "sha256": "697403aa648cda16d2ad5a9b306969731b2c2275bafcea29e3fd351370aa9b92"},
 }
 
 
@@ -534,11 +534,11 @@ def main():
         return None if ts is None else {"mean": round(float(np.mean(ts)), 4), "median": round(float(np.median(ts)), 4),
                                         "min": round(float(np.min(ts)), 4), "max": round(float(np.max(ts)), 4)}
 
-    # dominant launch by time: fa_bwd (its kernels bwd_prep, bwd_dkdv and bwd_dq run
-    # back to back on the stream and are timed together, as one launch of the
-    # backward) or fa_fwd (one kernel, fwd_bf16_kernel)
+    # dominant launch by time: fa_bwd (its kernels bwd_dq and bwd_dkdv run back to
+    # back on the stream and are timed together, as one launch of the backward) or
+    # fa_fwd (one kernel, fwd_bf16_kernel)
     if do_bwd and (not do_fwd or bwd_ms >= fwd_ms):
-        dom, dom_ms, dom_flops, which = "fa_bwd_ex (bwd_prep + bwd_dkdv + bwd_dq)", bwd_ms, f_bwd, "bwd"
+        dom, dom_ms, dom_flops, which = "fa_bwd_ex (bwd_dq + bwd_dkdv)", bwd_ms, f_bwd, "bwd"
     else:
         dom, dom_ms, dom_flops, which = "fa_fwd_ex (fwd_bf16_kernel)", fwd_ms, f_fwd, "fwd"
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
