@@ -8,7 +8,9 @@ the kernel's arithmetic:
   * the scores: one v_mfma_f32_32x32x64_f8f6f4 sums its 64 products with an error
     of at most 2^-11.2 of its largest product (measured on gfx950 with random e4m3
     operands whose magnitudes spread over e^0 .. e^8; the accumulation onto C adds
-    none), so with d/64 chained MFMAs a score is off by at most
+    none; AMD's documents do not state it, so test_fp8_score_accumulation_property
+    checks it through the library on every run), so with d/64 chained MFMAs a score
+    is off by at most
     delta_i = 2^-10 (d/64) |scale| max|q_i| max|k| (a margin of about 2 over the
     measurement); that moves lse by at most delta_i and every P by a factor within
     e^(+-delta_i), hence O by at most 2 (e^delta_i - 1) sum_j P_ij |v_j| / l_i;
@@ -205,3 +207,41 @@ def test_incoherent_processing_on_gpu():
     e_rot = float(np.sqrt(np.mean((host(o_rot) - exact) ** 2)))
     report("fp8 incoherent processing", rmse_plain=e_plain, rmse_rotated=e_rot)
     assert e_rot < 0.8 * e_plain
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_score_accumulation_property(d):
+    """The score term of the forward gate rests on how v_mfma_f32_32x32x64_f8f6f4 sums its
+    64 products, which AMD's documents do not state.  This checks that property through the
+    library itself: a row with a single key has P = 1 and l = 1, so its lse is exactly
+    |scale| times the kernel's own fp32 score (the quantisation scales are powers of two).
+    With codes whose magnitudes spread over e^0 .. e^8 inside a row, the score error of
+    every row must stay within 2^-10 (d/64) max|q| max|k|, the bound the gate assumes; the
+    report gives the error in units of the summed largest product of each 64-product MFMA
+    (2^-11.4 at d = 64 and 2^-12.1 at d = 128 on these inputs).
+    """
+    B, H = 16, 32
+    rng = np.random.default_rng(np.random.SeedSequence([35, 930, d]))
+
+    def spread(shape):
+        return (rng.choice([-1.0, 1.0], size=shape) * np.exp(rng.uniform(0.0, 8.0, size=shape))).astype(np.float32)
+
+    q8 = of8.quantize(spread((B, H, 1, d)))
+    k8 = of8.quantize(spread((B, H, 1, d)))
+    v8 = of8.quantize(spread((B, H, 1, d)))
+    (qc, qs), (kc, ks), (vc, vs) = q8, k8, v8
+    _, lse = api.forward_fp8(_u8(qc), _f32(qs), _u8(kc), _f32(ks), _u8(vc), _f32(vs), 1.0, False)
+    torch.cuda.synchronize()
+    dq = of8.dequantize(qc, qs)[:, :, 0]  # [B, H, d], exact in fp64
+    dk = of8.dequantize(kc, ks)[:, :, 0]
+    prod = dq * dk
+    exact = prod.sum(axis=-1)
+    err = np.abs(host(lse)[:, :, 0].astype(np.float64) - exact)
+    chunks = prod.reshape(B, H, d // 64, 64)
+    maxprod = np.abs(chunks).max(axis=-1).sum(axis=-1)              # sum over the chained MFMAs
+    gate_term = 2.0 ** -10 * (d / 64) * np.abs(dq).max(-1) * np.abs(dk).max(-1)
+    fp32_slack = 2.0 ** -21 * np.abs(prod).sum(axis=-1)             # the scaling multiplies after the MFMA
+    ratio = float((err / maxprod).max())
+    report(f"fp8 score accumulation d={d}", err_over_maxprod_log2=float(np.log2(max(ratio, 2.0 ** -40))),
+           err_over_gate=float((err / (gate_term + fp32_slack)).max()))
+    assert np.all(err <= gate_term + fp32_slack), float((err / (gate_term + fp32_slack)).max())
