@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from exact_attention_35_amd import api, inputs
-from gpu_util import TOL_BF16, TOL_F32, TOL_LSE, announce, dev, host, max_err, report
+from gpu_util import bf16_store_ratio, TOL_BF16, TOL_F32, TOL_LSE, announce, dev, host, max_err, report
 
 pytestmark = pytest.mark.gpu
 
@@ -142,15 +142,17 @@ def test_backward_scale_values(scale):
 
 
 def test_bf16_gradient_outputs():
-    """bf16 gradients carry one extra rounding of the stored value; gate at twice the fp32-output bound."""
+    """bf16 gradients carry one extra rounding of the stored value: the gate is the fp32-output
+    tolerance plus that rounding, elementwise (gpu_util.bf16_store_ratio)."""
     announce("bwd bf16 grads")
     q, k, v, do = inputs.random_case(14, 2, 2, 512, 64, "bf16", backward=True)
     scale = api.default_scale(64)
     _, _, dq, dk, dv = run(q, k, v, do, BF, scale, True, grad_dtype=BF)
     rdq, rdk, rdv = oracle.backward(q, k, v, do, scale, True)
     e = dict(dq=max_err(dq, rdq), dk=max_err(dk, rdk), dv=max_err(dv, rdv))
-    report("bwd bf16 grads", **e)
-    assert max(e.values()) <= 2 * TOL_BF16
+    r = dict(dq=bf16_store_ratio(dq, rdq), dk=bf16_store_ratio(dk, rdk), dv=bf16_store_ratio(dv, rdv))
+    report("bwd bf16 grads", **e, **{k_ + "_over_gate": v_ for k_, v_ in r.items()})
+    assert max(r.values()) <= 1.0, r
 
 
 def test_backward_invariants():
@@ -173,5 +175,5 @@ def test_autograd_wrapper():
     torch.cuda.synchronize()
     scale = api.default_scale(64)
     rdq, rdk, rdv = oracle.backward(q, k, v, do, scale, True)
-    for g, r in ((tq.grad, rdq), (tk.grad, rdk), (tv.grad, rdv)):
-        assert max_err(host(g), r) <= 2 * TOL_BF16
+    for g, r in ((tq.grad, rdq), (tk.grad, rdk), (tv.grad, rdv)):  # bf16 gradients
+        assert bf16_store_ratio(host(g), r) <= 1.0

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from exact_attention_35_amd import api, inputs
-from gpu_util import TOL_BF16, TOL_LSE, announce, dev, host, max_err, report
+from gpu_util import bf16_store_ratio, TOL_BF16, TOL_LSE, announce, dev, host, max_err, report
 
 pytestmark = pytest.mark.gpu
 
@@ -144,7 +144,9 @@ def test_blocksparse_backward_many_windows_bf16_gradients():
                 dk=max_err(host(dk), rk), dv=max_err(host(dv), rv))
     report(f"sparse N={n} d={d} bf16 gradients", **errs)
     assert errs["o"] <= TOL_BF16 and errs["lse"] <= TOL_LSE
-    assert max(errs["dq"], errs["dk"], errs["dv"]) <= 2 * TOL_BF16
+    ratios = [bf16_store_ratio(host(g), r) for g, r in ((dq, rq), (dk, rk), (dv, rv))]
+    report(f"sparse N={n} d={d} bf16 gradients, over the bf16-store gate", dq=ratios[0], dk=ratios[1], dv=ratios[2])
+    assert max(ratios) <= 1.0, ratios
 
 
 def test_autograd_wrapper_with_block_mask():
@@ -168,8 +170,8 @@ def test_autograd_wrapper_with_block_mask():
         assert torch.equal(g, e)
     scale = api.default_scale(d)
     rq, rk, rv = oracle.backward(q, k, v, do, scale, True, mask, inputs.MASK_BLOCK)
-    for g, r in ((tq.grad, rq), (tk.grad, rk), (tv.grad, rv)):
-        assert max_err(host(g), r) <= 2 * TOL_BF16
+    for g, r in ((tq.grad, rq), (tk.grad, rk), (tv.grad, rv)):  # bf16 gradients
+        assert bf16_store_ratio(host(g), r) <= 1.0
 
 
 def test_blocksparse_64k_backward_sampled():

@@ -44,10 +44,9 @@ def _run_case(seed, B, H, hkv, N, d, causal, masked):
     for got, want in zip((dq, dk, dv), ref):
         assert torch.equal(got, want)
     rq, rk, rv = oracle.backward(q, k, v, do, scale, causal, block_mask=mask_np)
-    g = H // hkv
     e = dict(dq=max_err(host(dq), rq), dk=max_err(host(dk), rk), dv=max_err(host(dv), rv))
     report(f"noalloc N={N} d={d} H_kv={hkv}", **e)
-    assert e["dq"] <= TOL_BF16 and max(e["dk"], e["dv"]) <= TOL_BF16 * np.sqrt(g)
+    assert max(e.values()) <= TOL_BF16, e
 
 
 def test_two_calls_in_a_row_second_smaller():
