@@ -389,9 +389,15 @@ def profile_summary(d):
     from collections import defaultdict
 
     lines = []
+    def query(con, sql):
+        try:
+            return con.execute(sql).fetchall()
+        except sqlite3.OperationalError:  # a results database without that view
+            return []
+
     for f in sorted(glob.glob(os.path.join(d, "**", "*results.db"), recursive=True)):
         con = sqlite3.connect(f)
-        rows = con.execute("select name, duration from kernels").fetchall()
+        rows = query(con, "select name, duration from kernels")
         if rows:
             per = defaultdict(list)
             for name, dur in rows:
@@ -403,7 +409,7 @@ def profile_summary(d):
                 sv = sorted(v)
                 lines.append(f"  {len(v):>5} {sum(v) / len(v):10.1f} {sv[len(sv) // 2]:10.1f} {sv[0]:10.1f} "
                              f"{sv[-1]:10.1f} {100.0 * sum(v) / total:6.2f}  {name[:90]}")
-        crow = con.execute("select dispatch_id, kernel_name, counter_name, value from counters_collection").fetchall()
+        crow = query(con, "select dispatch_id, kernel_name, counter_name, value from counters_collection")
         if crow:
             disp = defaultdict(float)
             names = {}
