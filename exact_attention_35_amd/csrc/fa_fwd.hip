@@ -206,7 +206,9 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   const int wave_q0 = SPARSE ? 128 * (hs == 0 ? mrows.x : mrows.y) + 32 * (2 * (wg & 1) + grp)
                              : q_first + 32 * (2 * wg + grp);
   const int qrow = wave_q0 + l32;
-  const int wi = SPARSE ? (wg & 1) : wg;  // this wave's share of a tile load
+  // this wave's share of a tile load, made wave-uniform so that the loads' LDS
+  // destinations (M0) are formed in scalar registers rather than read out of VGPRs
+  const int wi = __builtin_amdgcn_readfirstlane(SPARSE ? (wg & 1) : wg);
   unsigned short* const kb0 = kbuf_0 + hs * C::TILE;
   unsigned short* const kb1 = kbuf_1 + hs * C::TILE;
   unsigned short* const kb2 = kbuf_2 + hs * C::TILE;
