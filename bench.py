@@ -345,11 +345,11 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel writing o, o_lo and lse (fa_fwd_ex)
-    "fwd": {"fetch_kib": 256120.6, "write_kib": 133294.5,
+    "fwd": {"fetch_kib": 243607.7, "write_kib": 133398.5,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "1ccd677341c99754bf7f9e716d4edf4f5b6cc487421a52eacd58eab5dbd438f6"},
+            "sha256": "843d36a9f4ab1a62ab749dc9bb0b8a7d61eec29edbbb492111bcc6cdc61dc4ad"},
     # bwd_dq_kernel (also reading o, o_lo for D) + bwd_dkdv_kernel (fa_bwd_ex)
-    "bwd": {"fetch_kib": 384759.2 + 362549.4, "write_kib": 133120.0 + 262144.0,
+    "bwd": {"fetch_kib": 397737.8 + 362963.0, "write_kib": 133120.0 + 262144.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
             "sha256": "697403aa648cda16d2ad5a9b306969731b2c2275bafcea29e3fd351370aa9b92"},
 }
