@@ -345,11 +345,11 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel writing o, o_lo and lse (fa_fwd_ex)
-    "fwd": {"fetch_kib": 243607.7, "write_kib": 133398.5,
+    "fwd": {"fetch_kib": 245030.6, "write_kib": 133320.8,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "843d36a9f4ab1a62ab749dc9bb0b8a7d61eec29edbbb492111bcc6cdc61dc4ad"},
+            "sha256": "4f881fd332063be4af1e13e70554549859d51352eb90472b78dc57f83ba30c51"},
     # bwd_dq_kernel (also reading o, o_lo for D) + bwd_dkdv_kernel (fa_bwd_ex)
-    "bwd": {"fetch_kib": 397737.8 + 362963.0, "write_kib": 133120.0 + 262144.0,
+    "bwd": {"fetch_kib": 387970.5 + 363117.3, "write_kib": 133120.0 + 262144.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
             "sha256": "697403aa648cda16d2ad5a9b306969731b2c2275bafcea29e3fd351370aa9b92"},
 }

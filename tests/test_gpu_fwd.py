@@ -91,6 +91,28 @@ def test_edge_lengths_bf16(d, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_causal_around_short_sequence_limit(d):
+    """Causal sequences of up to 2048 keys run on the 128-query, 4-wave forward kernel and
+    longer ones on the 256-query, 8-wave kernel: both sides of that limit, with ragged tails.
+    The train-mode forward (with the low-order part of O) must give the same o and lse bit for
+    bit, and o + o_lo must stay within half the bf16 tolerance of the oracle."""
+    scale = api.default_scale(d)
+    for n in (2047, 2048, 2049, 2177):
+        announce(f"fwd bf16 causal N={n} d={d}")
+        q, k, v, _ = inputs.random_case(37, 1, 2, n, d, "bf16", mult=1.5)
+        tq, tk, tv = dev(q, BF), dev(k, BF), dev(v, BF)
+        o, lse = api.forward(tq, tk, tv, scale, True)
+        o2, lse2, o_lo = api.forward_train(tq, tk, tv, scale, True)
+        torch.cuda.synchronize()
+        ro, rl = oracle.forward(q, k, v, scale, True)
+        eo, el = max_err(host(o), ro), max_err(host(lse), rl)
+        e_full = max_err(host(o2) + host(o_lo), ro)
+        report(f"causal N={n} d={d}", o=eo, lse=el, o_plus_lo=e_full)
+        assert torch.equal(o, o2) and torch.equal(lse, lse2), n
+        assert eo <= TOL_BF16 and el <= TOL_LSE and e_full <= TOL_BF16 / 2, n
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_edge_lengths_f32(d, causal):
     for n in (1, 5, 64, 65, 200):
