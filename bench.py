@@ -345,13 +345,13 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel writing o, o_lo and lse (fa_fwd_ex)
-    "fwd": {"fetch_kib": 245030.6, "write_kib": 133320.8,
+    "fwd": {"fetch_kib": 243544.0, "write_kib": 133246.0,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "4f881fd332063be4af1e13e70554549859d51352eb90472b78dc57f83ba30c51"},
+            "sha256": "c6362168b0f19fdf44dfc963b58bf98d1b423df85f42e34e2ab32f3fd5281768"},
     # bwd_dq_kernel (also reading o, o_lo for D) + bwd_dkdv_kernel (fa_bwd_ex)
-    "bwd": {"fetch_kib": 387970.5 + 363117.3, "write_kib": 133120.0 + 262144.0,
+    "bwd": {"fetch_kib": 390166.3 + 363143.6, "write_kib": 133120.0 + 262144.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "697403aa648cda16d2ad5a9b306969731b2c2275bafcea29e3fd351370aa9b92"},
+            "sha256": "652761283cc114a66ede34fc5c7eb9afdf4967a94977ef98f3cac55f4c62dbd6"},
 }
 
 

@@ -14,7 +14,9 @@
 //     its query's dO row, so it first forms D and lse log2(e) (+inf for a row
 //     with no visible key, so that its P is 0) and stores them as one float2
 //     per row; it then streams K and V tiles through LDS and accumulates dQ in
-//     registers;
+//     registers (causal sequences of up to 2048 keys: bwd_dq_short_kernel, 128
+//     queries and 4 waves per workgroup, two workgroups per CU, the same
+//     arithmetic);
 //   * bwd_dkdv_kernel: one workgroup owns 128 keys; it streams 64-query tiles
 //     of Q and dO (and the stored row pairs) through LDS and accumulates dK,
 //     dV in registers.
@@ -163,6 +165,87 @@ __device__ __forceinline__ void sched_dq_gemm() {
   for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
+// This lane's query: Q and dO rows as MFMA B fragments (Q negated when the scale
+// is), D = rowsum(dO * O) with O taken as o + o_lo when the low-order part is given
+// (each half-wave sums its half of the row), and lse log2 e; the pair (lse log2 e, -D)
+// is also stored for the dK/dV kernel, which runs next.  Returns (lse log2 e, D);
+// rows past N read zeros and get lse log2 e = +inf, so their P is 0, as is that of a
+// row with no visible key.
+template <int D>
+__device__ __forceinline__ float2 dq_row_setup(const BwdBf16Args& a, BufRes qres, BufRes dores, size_t hoff,
+                                               unsigned int head_bytes, int bh, int qrow, int half,
+                                               bf16x8 (&qf)[D / 16], bf16x8 (&dof)[D / 16]) {
+  const int N = a.N;
+  {
+    const unsigned int sign = a.neg ? 0x80008000u : 0u;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const unsigned int off = (unsigned int)(qrow * D + 16 * c + 8 * half) * 2;  // rows past N: zeros
+      uint4 u = buf_load16(qres, off);
+      u.x ^= sign;
+      u.y ^= sign;
+      u.z ^= sign;
+      u.w ^= sign;
+      qf[c] = as_bf16x8(u);
+      dof[c] = as_bf16x8(buf_load16(dores, off));
+    }
+  }
+  float dpart = 0.f;
+  {
+    const BufRes ores = make_buf(a.o + hoff, head_bytes);
+    const bool with_lo = a.olo != nullptr;
+    const BufRes lres = make_buf(with_lo ? a.olo + hoff : a.o + hoff, head_bytes);
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      const unsigned int off = (unsigned int)(qrow * D + 16 * c + 8 * half) * 2;  // rows past N: zeros
+      const uint4 ov = buf_load16(ores, off);
+      const uint4 lv = with_lo ? buf_load16(lres, off) : zero_uint4();
+      const uint4 gv = as_uint4(dof[c]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float g = bf16_bits_to_float(bf16_lane_of(gv, e));
+        dpart = fmaf(bf16_bits_to_float(bf16_lane_of(ov, e)), g,
+                     fmaf(bf16_bits_to_float(bf16_lane_of(lv, e)), g, dpart));
+      }
+    }
+  }
+  const float dlt = xhalf_sum(dpart);
+  float lse2 = INFINITY;
+  if (qrow < N) {
+    const float l = a.lse[(size_t)bh * N + qrow];
+    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;  // +inf: a row with no visible key has P = 0
+    if (half == 0) a.stats[(size_t)bh * N + qrow] = make_float2(lse2, -dlt);
+  }
+  return make_float2(lse2, dlt);
+}
+
+// Vector phase of the dQ kernels for key tile kt: P = exp2(S c - lse log2 e) and
+// dS = P (dP - D), overwriting s, packed to bf16 MFMA fragments.  MASKED zeroes dS
+// for keys past N and, causal, after the query (a separate copy, so that the common
+// path has no per-element selects).
+template <int BN, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void dq_make_ds(f32x16 (&s)[BN / 32], const f32x16 (&dp)[BN / 32], bf16x8 (&dsf)[BN / 16],
+                                           int kt, int N, int qrow, int half, float c, float lse2, float dlt) {
+#pragma unroll
+  for (int b = 0; b < BN / 32; ++b) {
+    // key = base + off with off = 16(r/8) + (r%8) a constant: compare off with per-lane bounds
+    const int base = kt * BN + 32 * b + 8 * half;
+    const int lim_n = N - base, lim_c = qrow - base;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -lse2));
+      float ds = p * (dp[b][r] - dlt);
+      if (MASKED) {
+        const int off = 16 * (r >> 3) + (r & 7);
+        ds = (off >= lim_n || (CAUSAL && off > lim_c)) ? 0.f : ds;
+      }
+      s[b][r] = ds;
+    }
+  }
+#pragma unroll
+  for (int t2 = 0; t2 < BN / 16; ++t2) dsf[t2] = pack_bf16(s[t2 >> 1], 8 * (t2 & 1));
+}
+
 // Block-sparse (SPARSE): as in the block-sparse forward, SIMDs 0-1 and 2-3 serve
 // the two 128-row mask rows of the workgroup's 256 queries, each walking its own
 // row's kept key tiles through its own half of every ring buffer.
@@ -288,51 +371,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   }
   barrier_ring<LPW>();  // V(1) may still be landing
 
-  // ---- this lane's query: Q and dO rows as MFMA B fragments, lse and D
   bf16x8 qf[D / 16], dof[D / 16];
-  {
-    const unsigned int sign = a.neg ? 0x80008000u : 0u;
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const unsigned int off = (unsigned int)(qrow * D + 16 * c + 8 * half) * 2;  // rows past N: zeros
-      uint4 u = buf_load16(qres, off);
-      u.x ^= sign;
-      u.y ^= sign;
-      u.z ^= sign;
-      u.w ^= sign;
-      qf[c] = as_bf16x8(u);
-      dof[c] = as_bf16x8(buf_load16(dores, off));
-    }
-  }
-  // D = rowsum(dO * O) of this lane's query (O taken as o + o_lo when the low-order part is
-  // given; each half-wave sums its half of the row) and lse log2 e; the pair is also stored
-  // for the dK/dV kernel, which runs next.  Rows past N: P = 0.
-  float dpart = 0.f;
-  {
-    const BufRes ores = make_buf(a.o + hoff, head_bytes);
-    const bool with_lo = a.olo != nullptr;
-    const BufRes lres = make_buf(with_lo ? a.olo + hoff : a.o + hoff, head_bytes);
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const unsigned int off = (unsigned int)(qrow * D + 16 * c + 8 * half) * 2;  // rows past N: zeros
-      const uint4 ov = buf_load16(ores, off);
-      const uint4 lv = with_lo ? buf_load16(lres, off) : zero_uint4();
-      const uint4 gv = as_uint4(dof[c]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float g = bf16_bits_to_float(bf16_lane_of(gv, e));
-        dpart = fmaf(bf16_bits_to_float(bf16_lane_of(ov, e)), g,
-                     fmaf(bf16_bits_to_float(bf16_lane_of(lv, e)), g, dpart));
-      }
-    }
-  }
-  const float dlt = xhalf_sum(dpart);
-  float lse2 = INFINITY;
-  if (qrow < N) {
-    const float l = a.lse[(size_t)bh * N + qrow];
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;  // +inf: a row with no visible key has P = 0
-    if (half == 0) a.stats[(size_t)bh * N + qrow] = make_float2(lse2, -dlt);
-  }
+  const float2 row = dq_row_setup<D>(a, qres, dores, hoff, head_bytes, bh, qrow, half, qf, dof);
+  const float lse2 = row.x, dlt = row.y;
   const KOffsets<D> ko = k_offsets<D>(l32, half);
   const KtOffsets<D> kto = kt_offsets<D>(lane);
   const float c = a.c;
@@ -353,32 +394,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
     sched_dq_gemm<D, BN>();
     __builtin_amdgcn_s_setprio(0);
   };
-  // the masked variant is a separate copy so that the common path has no per-element selects
-  auto vector_body = [&](int kt, auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(mask_tag)::value;
-#pragma unroll
-    for (int b = 0; b < NSB; ++b) {
-      // key = base + off with off = 16(r/8) + (r%8) a constant: compare off with per-lane bounds
-      const int base = kt * BN + 32 * b + 8 * half;
-      const int lim_n = N - base, lim_c = qrow - base;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -lse2));
-        float ds = p * (dp[b][r] - dlt);
-        if (MASKED) {
-          const int off = 16 * (r >> 3) + (r & 7);
-          ds = (off >= lim_n || (CAUSAL && off > lim_c)) ? 0.f : ds;
-        }
-        s[b][r] = ds;
-      }
-    }
-#pragma unroll
-    for (int t2 = 0; t2 < NPT; ++t2) dsf[t2] = pack_bf16(s[t2 >> 1], 8 * (t2 & 1));
-  };
   auto vector_phase = [&](int t) __attribute__((always_inline)) {
     const int kt = tile_at(t);
-    if (need_mask(kt)) vector_body(kt, std::true_type{});
-    else vector_body(kt, std::false_type{});
+    if (need_mask(kt)) dq_make_ds<BN, CAUSAL, true>(s, dp, dsf, kt, N, qrow, half, c, lse2, dlt);
+    else dq_make_ds<BN, CAUSAL, false>(s, dp, dsf, kt, N, qrow, half, c, lse2, dlt);
   };
 
   // Step t: buffers rotate with t mod 3.  kprev holds K(t-1), kcur K(t), vcur V(t);
@@ -415,6 +434,119 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
     step(t, kb2, kb0, kb1, vb0, vb2);
     if (t + 1 <= nsteps) step(t + 1, kb0, kb1, kb2, vb1, vb0);
     if (t + 2 <= nsteps) step(t + 2, kb1, kb2, kb0, vb2, vb1);
+  }
+  wait_dma();  // no LDS-direct load may outlive the workgroup
+
+  store_grad_rows<D>(a.dq, hoff, N, qrow, half, a.grad_bf16, dqacc, a.scale);
+}
+
+// ---------------------------------------------------------------------------
+// dQ kernel for short causal sequences: one workgroup = 128 queries of one
+// (b, h), 4 waves of 32 queries, one per SIMD.  Each wave runs G(t) and then E(t)
+// of the same step itself (the arithmetic of bwd_dq_kernel, so the results are the
+// same bit for bit).  K and V tiles go through rings of three buffers, K one step
+// and V two steps ahead; with 48 KB of LDS two workgroups share a CU, so that one's
+// prologue, pipeline fill and epilogue overlap the other's steady state.
+// ---------------------------------------------------------------------------
+template <int D, int BN, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_dq_short_kernel(BwdBf16Args a) {
+  using C = TileCfg<D, BN>;
+  constexpr int BM = 128;
+  constexpr int NSB = C::NSB;
+  constexpr int NPT = C::NPT;
+  constexpr int NDB = D / 32;
+  constexpr int LPW = C::TILE * 2 / 1024 / 4;  // 1 KB loads per wave per tile
+  __shared__ __align__(16) unsigned short kbuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_2[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_2[C::TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int N = a.N;
+  const int nqt = (N + BM - 1) / BM;
+  const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / a.BH) : (int)(blockIdx.x / a.BH);  // longest rows first
+  const int bh = (int)(blockIdx.x % a.BH);
+  const size_t hoff = (size_t)bh * (size_t)N * D;
+  const size_t kvoff = (size_t)(bh / a.group) * (size_t)N * D;  // grouped-query: shared K/V head
+  const unsigned int head_bytes = (unsigned int)N * D * 2;
+  const BufRes qres = make_buf(a.q + hoff, head_bytes);
+  const BufRes kres = make_buf(a.k + kvoff, head_bytes);
+  const BufRes vres = make_buf(a.v + kvoff, head_bytes);
+  const BufRes dores = make_buf(a.dO + hoff, head_bytes);
+
+  const int q_first = qt * BM;
+  const int wave_q0 = q_first + 32 * w;
+  const int qrow = wave_q0 + l32;
+  const int wi = __builtin_amdgcn_readfirstlane(w);  // this wave's share of a tile load
+  const int kend = CAUSAL ? min(N, q_first + BM) : N;
+  const int ntiles = (kend + BN - 1) / BN;
+  auto tile_at = [&](int t) __attribute__((always_inline)) -> int { return min(t, ntiles - 1); };
+  auto need_mask = [&](int kt) __attribute__((always_inline)) -> bool {
+    const int k_first = kt * BN;
+    return (k_first + BN > N) || (CAUSAL && k_first + BN - 1 > wave_q0);
+  };
+
+  // Every tile buffer starts as zeros: K(-1) is read (times dS = 0) by the first
+  // step, and rows past N (which the range-checked loads may leave unwritten) are
+  // multiplied by zeros, so they must hold finite values.
+  for (int i = tid; i < C::TILE / 8; i += 256) {
+    reinterpret_cast<uint4*>(kbuf_0)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(kbuf_1)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(kbuf_2)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(vbuf_0)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(vbuf_1)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(vbuf_2)[i] = zero_uint4();
+  }
+  barrier_lds();
+  dma_k<D, BN, 4>(kres, kbuf_0, tile_at(0), wi, lane);
+  dma_k<D, BN, 4>(vres, vbuf_0, tile_at(0), wi, lane);
+  dma_k<D, BN, 4>(vres, vbuf_1, tile_at(1), wi, lane);
+  barrier_ring<LPW>();  // K(0) and V(0) have landed; V(1) may still be landing
+
+  bf16x8 qf[D / 16], dof[D / 16];
+  const float2 row = dq_row_setup<D>(a, qres, dores, hoff, head_bytes, bh, qrow, half, qf, dof);
+  const float lse2 = row.x, dlt = row.y;
+  const KOffsets<D> ko = k_offsets<D>(l32, half);
+  const KtOffsets<D> kto = kt_offsets<D>(lane);
+  const float c = a.c;
+
+  f32x16 dqacc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dqacc[i] = zero16();
+  f32x16 s[NSB], dp[NSB];
+  bf16x8 dsf[NPT];
+#pragma unroll
+  for (int i = 0; i < NPT; ++i) dsf[i] = as_bf16x8(zero_uint4());
+
+  // Step t: buffers rotate with t mod 3; kprev holds K(t-1), kcur K(t), vcur V(t).
+  // The wave fetches K(t+1) into knext and V(t+2) into vnext2, runs G(t) and E(t),
+  // and ends the step once K(t+1) has landed everywhere (V(t+2) may still be
+  // landing).  At t = 0 the dQ product uses dS = 0; at t = ntiles the S and dP of a
+  // repeated tile are never used.
+  auto step = [&](int t, const unsigned short* kprev, const unsigned short* kcur, unsigned short* knext,
+                  const unsigned short* vcur, unsigned short* vnext2) __attribute__((always_inline)) {
+    dma_k<D, BN, 4>(kres, knext, tile_at(t + 1), wi, lane);
+    dma_k<D, BN, 4>(vres, vnext2, tile_at(t + 2), wi, lane);
+    kt_tile<D, BN>(kprev, kto, dsf, dqacc);
+    qk_pair_tile<D, BN>(kcur, vcur, ko, qf, dof, s, dp);
+    sched_dq_gemm<D, BN>();
+    if (t < ntiles) {
+      const int kt = tile_at(t);
+      if (need_mask(kt)) dq_make_ds<BN, CAUSAL, true>(s, dp, dsf, kt, N, qrow, half, c, lse2, dlt);
+      else dq_make_ds<BN, CAUSAL, false>(s, dp, dsf, kt, N, qrow, half, c, lse2, dlt);
+    }
+    barrier_ring<LPW>();
+  };
+  for (int t = 0; t <= ntiles; t += 3) {
+    step(t, kbuf_2, kbuf_0, kbuf_1, vbuf_0, vbuf_2);
+    if (t + 1 <= ntiles) step(t + 1, kbuf_0, kbuf_1, kbuf_2, vbuf_1, vbuf_0);
+    if (t + 2 <= ntiles) step(t + 2, kbuf_1, kbuf_2, kbuf_0, vbuf_2, vbuf_1);
   }
   wait_dma();  // no LDS-direct load may outlive the workgroup
 
@@ -975,6 +1107,12 @@ static void launch_prep_f32(const BwdParams& p, hipStream_t stream) {
                      static_cast<const float*>(p.dO), p.lse, reinterpret_cast<float2*>(p.stats), rows);
 }
 
+// Longest causal sequence whose dQ runs on bwd_dq_short_kernel.  Measured on MI355X
+// (bf16, 16 heads, whole backward): 3-7% faster at d = 64 for N of 512-2048 (15% at
+// one batch of N = 1024), 0.5-3% at d = 128; without causal masking it gains at most
+// 2% at d = 64 and loses 4% at d = 128.
+constexpr int kShortCausalN = 2048;
+
 template <int D, bool CAUSAL, bool SPARSE>
 static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   BwdBf16Args a;
@@ -1016,9 +1154,14 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
     akv.grad_bf16 = 0;
   }
   // the dQ kernel first: it also forms D and stores each row's (lse log2 e, -D) for the dK/dV kernel
-  const unsigned nqb = (unsigned)((p.N + 255) / 256);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, DQ_BN, CAUSAL, SPARSE>), dim3(nqb * (unsigned)a.BH), dim3(512), dyn_q, stream,
-                     a);
+  if (!SPARSE && CAUSAL && p.N <= kShortCausalN) {
+    const unsigned nqs = (unsigned)((p.N + 127) / 128);
+    hipLaunchKernelGGL((bwd_dq_short_kernel<D, DQ_BN, CAUSAL>), dim3(nqs * (unsigned)a.BH), dim3(256), 0, stream, a);
+  } else {
+    const unsigned nqb = (unsigned)((p.N + 255) / 256);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, DQ_BN, CAUSAL, SPARSE>), dim3(nqb * (unsigned)a.BH), dim3(512), dyn_q,
+                       stream, a);
+  }
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(nkb * (unsigned)a.BH), dim3(512), dyn_kv, stream,
                      akv);
 }

@@ -518,9 +518,13 @@ __global__ __launch_bounds__(256) void fwd_bf16_short_kernel(FwdKernelArgs a) {
 #pragma unroll
   for (int t = 0; t < NPT; ++t) pf[t] = as_bf16x8(zero_uint4());
 
-  // step 0 multiplies V buffer 1 by P = 0, so it must hold finite values; every
-  // other V buffer read has been filled by range-checked loads (zeros past N)
-  for (int i = tid; i < C::TILE / 8; i += 256) reinterpret_cast<uint4*>(vbuf_1)[i] = zero_uint4();
+  // V buffers start as zeros: step 0 multiplies buffer 1 by P = 0, and key rows
+  // past N (which the range-checked loads may leave unwritten) must hold finite
+  // values, since they are multiplied by P = 0 as well
+  for (int i = tid; i < C::TILE / 8; i += 256) {
+    reinterpret_cast<uint4*>(vbuf_0)[i] = zero_uint4();
+    reinterpret_cast<uint4*>(vbuf_1)[i] = zero_uint4();
+  }
   barrier_lds();
   dma_k<D, BN, 4>(kres, kbuf_0, tile_at(0), wi, lane);
   barrier_ring<0>();  // K(0) has landed
