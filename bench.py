@@ -345,13 +345,13 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel writing o, o_lo and lse (fa_fwd_ex)
-    "fwd": {"fetch_kib": 243544.0, "write_kib": 133246.0,
+    "fwd": {"fetch_kib": 247505.8, "write_kib": 133285.7,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "c6362168b0f19fdf44dfc963b58bf98d1b423df85f42e34e2ab32f3fd5281768"},
+            "sha256": "b500ea5613e3f2d226727de317954adbcec1d7d1e2465a9b019ffb538ea3fe07"},
     # bwd_dq_kernel (also reading o, o_lo for D) + bwd_dkdv_kernel (fa_bwd_ex)
-    "bwd": {"fetch_kib": 390166.3 + 363143.6, "write_kib": 133120.0 + 262144.0,
+    "bwd": {"fetch_kib": 387987.8 + 363396.1, "write_kib": 133120.0 + 262144.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "652761283cc114a66ede34fc5c7eb9afdf4967a94977ef98f3cac55f4c62dbd6"},
+            "sha256": "fbf596a865c87763b56c5956306fcb51da419dedc59cd5b419b6f2263bd35748"},
 }
 
 

@@ -15,8 +15,8 @@
 //     with no visible key, so that its P is 0) and stores them as one float2
 //     per row; it then streams K and V tiles through LDS and accumulates dQ in
 //     registers (causal sequences of up to 2048 keys: bwd_dq_short_kernel, 128
-//     queries and 4 waves per workgroup, two workgroups per CU, the same
-//     arithmetic);
+//     queries and 4 waves per workgroup, two or three workgroups per CU, the
+//     same arithmetic);
 //   * bwd_dkdv_kernel: one workgroup owns 128 keys; it streams 64-query tiles
 //     of Q and dO (and the stored row pairs) through LDS and accumulates dK,
 //     dV in registers.
@@ -444,12 +444,15 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
 // dQ kernel for short causal sequences: one workgroup = 128 queries of one
 // (b, h), 4 waves of 32 queries, one per SIMD.  Each wave runs G(t) and then E(t)
 // of the same step itself (the arithmetic of bwd_dq_kernel, so the results are the
-// same bit for bit).  K and V tiles go through rings of three buffers, K one step
-// and V two steps ahead; with 48 KB of LDS two workgroups share a CU, so that one's
-// prologue, pipeline fill and epilogue overlap the other's steady state.
+// same bit for bit for the same tile size).  K and V tiles go through rings of
+// three buffers, K one step and V two steps ahead.  Several workgroups share a CU,
+// so that one's prologue, pipeline fill and epilogue overlap another's steady
+// state: two at d = 128 (48 KB of LDS), three at d = 64, where 32-key tiles (24 KB)
+// let the kernel be held to 168 registers.
 // ---------------------------------------------------------------------------
 template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_dq_short_kernel(BwdBf16Args a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1, 8)))
+void bwd_dq_short_kernel(BwdBf16Args a) {
   using C = TileCfg<D, BN>;
   constexpr int BM = 128;
   constexpr int NSB = C::NSB;
@@ -1108,9 +1111,9 @@ static void launch_prep_f32(const BwdParams& p, hipStream_t stream) {
 }
 
 // Longest causal sequence whose dQ runs on bwd_dq_short_kernel.  Measured on MI355X
-// (bf16, 16 heads, whole backward): 3-7% faster at d = 64 for N of 512-2048 (15% at
-// one batch of N = 1024), 0.5-3% at d = 128; without causal masking it gains at most
-// 2% at d = 64 and loses 4% at d = 128.
+// (bf16, 16 heads, whole backward, against bwd_dq_kernel): about 8-11% faster at
+// d = 64 (32-key tiles) for N of 512-2048, 0.5-3% at d = 128; without causal masking
+// it gained at most 2% at d = 64 and lost 4% at d = 128 (with 64-key tiles).
 constexpr int kShortCausalN = 2048;
 
 template <int D, bool CAUSAL, bool SPARSE>
@@ -1154,10 +1157,17 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
     akv.grad_bf16 = 0;
   }
   // the dQ kernel first: it also forms D and stores each row's (lse log2 e, -D) for the dK/dV kernel
-  if (!SPARSE && CAUSAL && p.N <= kShortCausalN) {
-    const unsigned nqs = (unsigned)((p.N + 127) / 128);
-    hipLaunchKernelGGL((bwd_dq_short_kernel<D, DQ_BN, CAUSAL>), dim3(nqs * (unsigned)a.BH), dim3(256), 0, stream, a);
-  } else {
+  bool short_dq = false;
+  if constexpr (!SPARSE && CAUSAL) {
+    if (p.N <= kShortCausalN) {
+      short_dq = true;
+      const unsigned nqs = (unsigned)((p.N + 127) / 128);
+      constexpr int SBN = D == 64 ? 32 : DQ_BN;  // keys per tile: at d = 64, three workgroups per CU
+      hipLaunchKernelGGL((bwd_dq_short_kernel<D, SBN, CAUSAL>), dim3(nqs * (unsigned)a.BH), dim3(256), 0, stream,
+                         a);
+    }
+  }
+  if (!short_dq) {
     const unsigned nqb = (unsigned)((p.N + 255) / 256);
     hipLaunchKernelGGL((bwd_dq_kernel<D, DQ_BN, CAUSAL, SPARSE>), dim3(nqb * (unsigned)a.BH), dim3(512), dyn_q,
                        stream, a);

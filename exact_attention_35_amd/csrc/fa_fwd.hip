@@ -25,8 +25,8 @@
 // Grouped-query heads read K/V head bh / group.  Block-sparse: each half of the
 // workgroup lists the key tiles kept by its 128-row mask row and visits only
 // those.  Causal sequences of up to 2048 keys go to fwd_bf16_short_kernel
-// instead: 128 queries and 4 waves per workgroup, two workgroups per CU, the
-// same arithmetic.  fwd_f32_kernel is a plain fp32 kernel (one query per thread).
+// instead: 128 queries and 4 waves per workgroup, two to four workgroups per
+// CU, the same arithmetic.  fwd_f32_kernel is a plain fp32 kernel (one query per thread).
 #include <math.h>
 
 #include "fa_device.hpp"
@@ -453,9 +453,12 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
 // tile t.  With 64 KB of LDS two workgroups share a CU, so one's prologue,
 // pipeline fill and epilogue overlap the other's steady state: over a short key
 // range these fixed costs, and the wasted half of the diagonal tile under causal
-// masking, outweigh the MFMA/softmax overlap of the 8-wave kernel.
+// masking, outweigh the MFMA/softmax overlap of the 8-wave kernel.  At d = 64
+// with 64-key tiles (32 KB of LDS) the kernel is held to 128 registers, so that
+// four workgroups share a CU.
 template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_bf16_short_kernel(FwdKernelArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && BN == 64 ? 4 : 1, 8)))
+void fwd_bf16_short_kernel(FwdKernelArgs a) {
   using C = FwdCfg<D, BN>;
   constexpr int BM = 128;
   constexpr int NSB = C::NSB;
@@ -714,6 +717,11 @@ static hipError_t launch_fwd_f32_t(const FwdParams& p, hipStream_t stream) {
 // 512-2048, 0-6% at d = 128, and 3-15% slower from N = 4096 on; without causal
 // masking it is no faster at N <= 1024 and slower beyond.
 constexpr int kShortCausalN = 2048;
+// Smallest grid (workgroups) for which the d = 64 short kernel takes 64-key tiles
+// at four workgroups per CU rather than 128-key tiles at two: measured 11-19% faster
+// from 768 workgroups on (B = 8, H = 12, N = 1024: 37.6 -> 31.7 us) and 8% slower at
+// 256, where the CUs cannot be filled either way and the shorter tiles only add steps.
+constexpr long long kShortSmallTileGrid = 512;
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
   // an error left by an earlier, unrelated HIP call must not be reported as ours
@@ -723,9 +731,14 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     if (p.d == 64) return p.causal ? launch_fwd_f32_t<64, true>(p, stream) : launch_fwd_f32_t<64, false>(p, stream);
     return p.causal ? launch_fwd_f32_t<128, true>(p, stream) : launch_fwd_f32_t<128, false>(p, stream);
   }
-  // short causal sequences (N <= 2048): 128-query, 4-wave workgroups
-  if (!sparse && p.causal && p.N <= kShortCausalN)
-    return p.d == 64 ? launch_fwd_short_t<64, 128, true>(p, stream) : launch_fwd_short_t<128, 64, true>(p, stream);
+  // short causal sequences (N <= 2048): 128-query, 4-wave workgroups; at d = 64,
+  // 64-key tiles at four workgroups per CU once the grid has two per CU
+  if (!sparse && p.causal && p.N <= kShortCausalN) {
+    if (p.d == 128) return launch_fwd_short_t<128, 64, true>(p, stream);
+    const long long nwg = (long long)((p.N + 127) / 128) * p.B * p.H;
+    return nwg >= kShortSmallTileGrid ? launch_fwd_short_t<64, 64, true>(p, stream)
+                                      : launch_fwd_short_t<64, 128, true>(p, stream);
+  }
   // block-sparse: 8 KB tiles (64 keys at d = 64, 32 at d = 128), two streams per workgroup
   if (p.d == 64) {
     if (sparse)

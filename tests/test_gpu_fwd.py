@@ -112,6 +112,22 @@ def test_causal_around_short_sequence_limit(d):
         assert eo <= TOL_BF16 and el <= TOL_LSE and e_full <= TOL_BF16 / 2, n
 
 
+def test_short_causal_d64_large_grid():
+    """Short causal d = 64 forwards whose grid has at least 512 blocks of 128 queries take
+    64-key tiles at four workgroups per CU (smaller grids, 128-key tiles): two ragged shapes on
+    that path, every element against the oracle."""
+    for b, h, n in ((2, 16, 2047), (4, 32, 1000)):
+        assert -(-n // 128) * b * h >= 512
+        announce(f"fwd bf16 causal B={b} H={h} N={n} d=64")
+        q, k, v, _ = inputs.random_case(43, b, h, n, 64, "bf16", mult=1.5)
+        scale = api.default_scale(64)
+        o, lse = run_fwd(q, k, v, BF, scale, True)
+        ro, rl = oracle.forward(q, k, v, scale, True)
+        eo, el = max_err(o, ro), max_err(lse, rl)
+        report(f"causal B={b} H={h} N={n} d=64", o=eo, lse=el)
+        assert eo <= TOL_BF16 and el <= TOL_LSE, (b, h, n)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_edge_lengths_f32(d, causal):
