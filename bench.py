@@ -345,13 +345,13 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel writing o, o_lo and lse (fa_fwd_ex)
-    "fwd": {"fetch_kib": 247505.8, "write_kib": 133285.7,
+    "fwd": {"fetch_kib": 246617.3, "write_kib": 133203.7,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "b500ea5613e3f2d226727de317954adbcec1d7d1e2465a9b019ffb538ea3fe07"},
+            "sha256": "3f0889fc0f494f36cbc4ee9ba8f3326915c4d32d9e8dc38daecb064e6b08e06a"},
     # bwd_dq_kernel (also reading o, o_lo for D) + bwd_dkdv_kernel (fa_bwd_ex)
-    "bwd": {"fetch_kib": 387987.8 + 363396.1, "write_kib": 133120.0 + 262144.0,
+    "bwd": {"fetch_kib": 387513.4 + 363051.9, "write_kib": 133120.0 + 262144.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "fbf596a865c87763b56c5956306fcb51da419dedc59cd5b419b6f2263bd35748"},
+            "sha256": "8c4a68dd34eda9f8e7cfa5d89ff8b5dbc1911f2f83c3faf4a4779ed08bab764c"},
 }
 
 

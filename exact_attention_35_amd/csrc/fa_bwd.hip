@@ -14,9 +14,9 @@
 //     its query's dO row, so it first forms D and lse log2(e) (+inf for a row
 //     with no visible key, so that its P is 0) and stores them as one float2
 //     per row; it then streams K and V tiles through LDS and accumulates dQ in
-//     registers (causal sequences of up to 2048 keys: bwd_dq_short_kernel, 128
-//     queries and 4 waves per workgroup, two or three workgroups per CU, the
-//     same arithmetic);
+//     registers (at d = 64, and for causal sequences of up to 2048 keys at
+//     d = 128: bwd_dq_short_kernel, 128 queries and 4 waves per workgroup, two
+//     or three workgroups per CU, the same arithmetic);
 //   * bwd_dkdv_kernel: one workgroup owns 128 keys; it streams 64-query tiles
 //     of Q and dO (and the stored row pairs) through LDS and accumulates dK,
 //     dV in registers.
@@ -441,7 +441,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ kernel for short causal sequences: one workgroup = 128 queries of one
+// dQ kernel for short key ranges: one workgroup = 128 queries of one
 // (b, h), 4 waves of 32 queries, one per SIMD.  Each wave runs G(t) and then E(t)
 // of the same step itself (the arithmetic of bwd_dq_kernel, so the results are the
 // same bit for bit for the same tile size).  K and V tiles go through rings of
@@ -1110,10 +1110,12 @@ static void launch_prep_f32(const BwdParams& p, hipStream_t stream) {
                      static_cast<const float*>(p.dO), p.lse, reinterpret_cast<float2*>(p.stats), rows);
 }
 
-// Longest causal sequence whose dQ runs on bwd_dq_short_kernel.  Measured on MI355X
-// (bf16, 16 heads, whole backward, against bwd_dq_kernel): about 8-11% faster at
-// d = 64 (32-key tiles) for N of 512-2048, 0.5-3% at d = 128; without causal masking
-// it gained at most 2% at d = 64 and lost 4% at d = 128 (with 64-key tiles).
+// When bwd_dq_short_kernel serves the dQ of a dense bf16 backward (measured on MI355X,
+// bf16, 12-16 heads, whole backward against bwd_dq_kernel, interleaved on one box): at
+// d = 64 (32-key tiles, three workgroups per CU) always, causal or not (9-10% faster at
+// causal N = 512-2048, 4-7% without masking, 3-4% at 4K-8K, 14% on a grid of 256
+// workgroups, 1-2% at 16K-64K); at d = 128 (two per CU) for causal N <= 2048 (0-3%
+// faster, 12% on a grid of 128 workgroups), where without causal masking it lost 4%.
 constexpr int kShortCausalN = 2048;
 
 template <int D, bool CAUSAL, bool SPARSE>
@@ -1158,8 +1160,8 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   }
   // the dQ kernel first: it also forms D and stores each row's (lse log2 e, -D) for the dK/dV kernel
   bool short_dq = false;
-  if constexpr (!SPARSE && CAUSAL) {
-    if (p.N <= kShortCausalN) {
+  if constexpr (!SPARSE && (CAUSAL || D == 64)) {
+    if (D == 64 || p.N <= kShortCausalN) {
       short_dq = true;
       const unsigned nqs = (unsigned)((p.N + 127) / 128);
       constexpr int SBN = D == 64 ? 32 : DQ_BN;  // keys per tile: at d = 64, three workgroups per CU

@@ -24,9 +24,9 @@
 //   * epilogue: O = acc / l, lse = m * |scale| + ln l (natural log).
 // Grouped-query heads read K/V head bh / group.  Block-sparse: each half of the
 // workgroup lists the key tiles kept by its 128-row mask row and visits only
-// those.  Causal sequences of up to 2048 keys go to fwd_bf16_short_kernel
-// instead: 128 queries and 4 waves per workgroup, two to four workgroups per
-// CU, the same arithmetic.  fwd_f32_kernel is a plain fp32 kernel (one query per thread).
+// those.  Short key ranges (causal N <= 2048, and at d = 64 causal N <= 8192 or
+// N <= 4096) go to fwd_bf16_short_kernel instead: 128 queries and 4 waves per
+// workgroup, two to four workgroups per CU, the same arithmetic.  fwd_f32_kernel is a plain fp32 kernel (one query per thread).
 #include <math.h>
 
 #include "fa_device.hpp"
@@ -453,11 +453,11 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
 // tile t.  With 64 KB of LDS two workgroups share a CU, so one's prologue,
 // pipeline fill and epilogue overlap the other's steady state: over a short key
 // range these fixed costs, and the wasted half of the diagonal tile under causal
-// masking, outweigh the MFMA/softmax overlap of the 8-wave kernel.  At d = 64
-// with 64-key tiles (32 KB of LDS) the kernel is held to 128 registers, so that
-// four workgroups share a CU.
+// masking, outweigh the MFMA/softmax overlap of the 8-wave kernel.  With 64-key
+// tiles at d = 64 (32 KB of LDS) the kernel is held to 128 registers, so that four
+// workgroups share a CU; with 32-key tiles at d = 128 (32 KB) to 168, three per CU.
 template <int D, int BN, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && BN == 64 ? 4 : 1, 8)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && BN == 64 ? 4 : (D == 128 && BN == 32 ? 3 : 1), 8)))
 void fwd_bf16_short_kernel(FwdKernelArgs a) {
   using C = FwdCfg<D, BN>;
   constexpr int BM = 128;
@@ -712,15 +712,20 @@ static hipError_t launch_fwd_f32_t(const FwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Longest causal sequence served by fwd_bf16_short_kernel.  Measured on MI355X
-// (bf16, 16 heads): it is 6-23% faster than fwd_bf16_kernel at d = 64 for N of
-// 512-2048, 0-6% at d = 128, and 3-15% slower from N = 4096 on; without causal
-// masking it is no faster at N <= 1024 and slower beyond.
+// When fwd_bf16_short_kernel serves a dense bf16 forward (measured on MI355X, bf16,
+// 12-16 heads, against fwd_bf16_kernel, interleaved on one box):
+//  * d = 64, 64-key tiles, four workgroups per CU: causal N <= 8192 on grids of at
+//    least 512 workgroups (21-37% faster at N = 512-2048, 15% at 4096, 4% at 8192;
+//    1-3% slower from 16K on); without causal masking N <= 4096 on any grid (6-23%
+//    faster, 17-20% on grids of 256 workgroups; 3% slower at 16K-32K);
+//  * d = 64, 128-key tiles, two per CU: causal N <= 2048 on smaller grids (21% faster
+//    on 256 workgroups, where the 64-key tiles were 8% slower still: the CUs cannot be
+//    filled either way and the shorter tiles only add steps);
+//  * d = 128, 32-key tiles, three per CU: causal N <= 2048 (9-16% faster, 23% on a grid
+//    of 128 workgroups; even at N = 4096); without causal masking 3-20% slower.
 constexpr int kShortCausalN = 2048;
-// Smallest grid (workgroups) for which the d = 64 short kernel takes 64-key tiles
-// at four workgroups per CU rather than 128-key tiles at two: measured 11-19% faster
-// from 768 workgroups on (B = 8, H = 12, N = 1024: 37.6 -> 31.7 us) and 8% slower at
-// 256, where the CUs cannot be filled either way and the shorter tiles only add steps.
+constexpr int kShortD64CausalN = 8192;
+constexpr int kShortD64N = 4096;
 constexpr long long kShortSmallTileGrid = 512;
 
 hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
@@ -731,13 +736,16 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     if (p.d == 64) return p.causal ? launch_fwd_f32_t<64, true>(p, stream) : launch_fwd_f32_t<64, false>(p, stream);
     return p.causal ? launch_fwd_f32_t<128, true>(p, stream) : launch_fwd_f32_t<128, false>(p, stream);
   }
-  // short causal sequences (N <= 2048): 128-query, 4-wave workgroups; at d = 64,
-  // 64-key tiles at four workgroups per CU once the grid has two per CU
-  if (!sparse && p.causal && p.N <= kShortCausalN) {
-    if (p.d == 128) return launch_fwd_short_t<128, 64, true>(p, stream);
+  // short key ranges: 128-query, 4-wave workgroups, several per CU
+  if (!sparse) {
     const long long nwg = (long long)((p.N + 127) / 128) * p.B * p.H;
-    return nwg >= kShortSmallTileGrid ? launch_fwd_short_t<64, 64, true>(p, stream)
-                                      : launch_fwd_short_t<64, 128, true>(p, stream);
+    if (p.d == 64) {
+      if (p.causal ? (p.N <= kShortD64CausalN && nwg >= kShortSmallTileGrid) : p.N <= kShortD64N)
+        return p.causal ? launch_fwd_short_t<64, 64, true>(p, stream) : launch_fwd_short_t<64, 64, false>(p, stream);
+      if (p.causal && p.N <= kShortCausalN) return launch_fwd_short_t<64, 128, true>(p, stream);
+    } else if (p.causal && p.N <= kShortCausalN) {
+      return launch_fwd_short_t<128, 32, true>(p, stream);
+    }
   }
   // block-sparse: 8 KB tiles (64 keys at d = 64, 32 at d = 128), two streams per workgroup
   if (p.d == 64) {

@@ -150,9 +150,10 @@ def test_edge_lengths_bf16(d, causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_causal_around_short_sequence_limit(d):
-    """dQ of causal sequences of up to 2048 keys runs on the 128-query, 4-wave kernel and of
-    longer ones on the 256-query, 8-wave kernel: both sides of that limit, ragged, with the
-    forward's low-order part of O (as the benchmark runs it) and bf16 gradients."""
+    """At d = 128 the dQ of causal sequences of up to 2048 keys runs on the 128-query, 4-wave
+    kernel and of longer ones on the 256-query, 8-wave kernel (at d = 64 the 4-wave kernel
+    serves both): both sides of that limit, ragged, with the forward's low-order part of O
+    (as the benchmark runs it) and bf16 gradients."""
     scale = api.default_scale(d)
     for n in (2047, 2049):
         announce(f"bwd bf16 causal N={n} d={d}")
@@ -168,6 +169,20 @@ def test_causal_around_short_sequence_limit(d):
         r = dict(dq=bf16_store_ratio(dq, rdq), dk=bf16_store_ratio(dk, rdk), dv=bf16_store_ratio(dv, rdv))
         report(f"bwd causal N={n} d={d}", **e, **{k_ + "_over_gate": v_ for k_, v_ in r.items()})
         assert max(r.values()) <= 1.0, (n, d, r)
+
+
+@pytest.mark.parametrize("n, causal", [(4100, True), (3000, False)])
+def test_d64_backward_longer_sequences(n, causal):
+    """At d = 64 the 128-query, 4-wave dQ kernel serves every length, with and without causal
+    masking: two ragged lengths past 2048 against the oracle (fp32 gradients)."""
+    announce(f"bwd bf16 N={n} d=64 causal={causal}")
+    q, k, v, do = inputs.random_case(47, 1, 2, n, 64, "bf16", backward=True)
+    scale = api.default_scale(64)
+    _, _, dq, dk, dv = run(q, k, v, do, BF, scale, causal)
+    rdq, rdk, rdv = oracle.backward(q, k, v, do, scale, causal)
+    e = dict(dq=max_err(dq, rdq), dk=max_err(dk, rdk), dv=max_err(dv, rdv))
+    report(f"bwd N={n} d=64 causal={causal}", **e)
+    assert max(e.values()) <= TOL_BF16, e
 
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -92,8 +92,9 @@ def test_edge_lengths_bf16(d, causal):
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_causal_around_short_sequence_limit(d):
-    """Causal sequences of up to 2048 keys run on the 128-query, 4-wave forward kernel and
-    longer ones on the 256-query, 8-wave kernel: both sides of that limit, with ragged tails.
+    """Causal sequences of up to 2048 keys run on the 128-query, 4-wave forward kernel and, on
+    this small grid, longer ones on the 256-query, 8-wave kernel: both sides of that limit,
+    with ragged tails.
     The train-mode forward (with the low-order part of O) must give the same o and lse bit for
     bit, and o + o_lo must stay within half the bf16 tolerance of the oracle."""
     scale = api.default_scale(d)
@@ -112,20 +113,23 @@ def test_causal_around_short_sequence_limit(d):
         assert eo <= TOL_BF16 and el <= TOL_LSE and e_full <= TOL_BF16 / 2, n
 
 
-def test_short_causal_d64_large_grid():
-    """Short causal d = 64 forwards whose grid has at least 512 blocks of 128 queries take
-    64-key tiles at four workgroups per CU (smaller grids, 128-key tiles): two ragged shapes on
-    that path, every element against the oracle."""
-    for b, h, n in ((2, 16, 2047), (4, 32, 1000)):
-        assert -(-n // 128) * b * h >= 512
-        announce(f"fwd bf16 causal B={b} H={h} N={n} d=64")
-        q, k, v, _ = inputs.random_case(43, b, h, n, 64, "bf16", mult=1.5)
-        scale = api.default_scale(64)
-        o, lse = run_fwd(q, k, v, BF, scale, True)
-        ro, rl = oracle.forward(q, k, v, scale, True)
-        eo, el = max_err(o, ro), max_err(lse, rl)
-        report(f"causal B={b} H={h} N={n} d=64", o=eo, lse=el)
-        assert eo <= TOL_BF16 and el <= TOL_LSE, (b, h, n)
+@pytest.mark.parametrize("b, h, n, causal", [(2, 16, 2047, True), (4, 32, 1000, True), (1, 16, 4100, True),
+                                              (2, 8, 3000, False)])
+def test_short_kernel_d64_64key_tiles(b, h, n, causal):
+    """d = 64 forwards that take the 128-query kernel with 64-key tiles at four workgroups per
+    CU: causal with N <= 8192 on grids of at least 512 blocks of 128 queries, and without
+    causal masking N <= 4096 on any grid.  Ragged shapes on that path, every element against
+    the oracle."""
+    if causal:
+        assert -(-n // 128) * b * h >= 512 and n <= 8192
+    announce(f"fwd bf16 B={b} H={h} N={n} d=64 causal={causal}")
+    q, k, v, _ = inputs.random_case(43, b, h, n, 64, "bf16", mult=1.5)
+    scale = api.default_scale(64)
+    o, lse = run_fwd(q, k, v, BF, scale, causal)
+    ro, rl = oracle.forward(q, k, v, scale, causal)
+    eo, el = max_err(o, ro), max_err(lse, rl)
+    report(f"B={b} H={h} N={n} d=64 causal={causal}", o=eo, lse=el)
+    assert eo <= TOL_BF16 and el <= TOL_LSE
 
 
 @pytest.mark.parametrize("d", [64, 128])
