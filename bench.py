@@ -345,13 +345,13 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel writing o, o_lo and lse (fa_fwd_ex)
-    "fwd": {"fetch_kib": 246617.3, "write_kib": 133203.7,
+    "fwd": {"fetch_kib": 240136.6, "write_kib": 133320.5,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "3f0889fc0f494f36cbc4ee9ba8f3326915c4d32d9e8dc38daecb064e6b08e06a"},
+            "sha256": "c1d6ed5f4fa1e168c1d3973d216f9aa88c2055dc65d1e6f92c4f87b4abcf68f5"},
     # bwd_dq_kernel (also reading o, o_lo for D) + bwd_dkdv_kernel (fa_bwd_ex)
-    "bwd": {"fetch_kib": 387513.4 + 363051.9, "write_kib": 133120.0 + 262144.0,
+    "bwd": {"fetch_kib": 389008.9 + 363109.1, "write_kib": 133120.0 + 262144.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "8c4a68dd34eda9f8e7cfa5d89ff8b5dbc1911f2f83c3faf4a4779ed08bab764c"},
+            "sha256": "e706488eea988eab24b30fd35de4380915a578336375e3838de7df2c9eedf61b"},
 }
 
 

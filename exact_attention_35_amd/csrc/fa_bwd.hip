@@ -246,27 +246,22 @@ __device__ __forceinline__ void dq_make_ds(f32x16 (&s)[BN / 32], const f32x16 (&
   for (int t2 = 0; t2 < BN / 16; ++t2) dsf[t2] = pack_bf16(s[t2 >> 1], 8 * (t2 & 1));
 }
 
-// Block-sparse (SPARSE): as in the block-sparse forward, SIMDs 0-1 and 2-3 serve
-// the two 128-row mask rows of the workgroup's 256 queries, each walking its own
-// row's kept key tiles through its own half of every ring buffer.
-template <int D, int BN, bool CAUSAL, bool SPARSE>
+// (Block-sparse dQ runs on bwd_dq_short_kernel, whose 128 queries are one mask row.)
+template <int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   using C = TileCfg<D, BN>;
   constexpr int BM = 256;
   constexpr int NSB = C::NSB;
   constexpr int NPT = C::NPT;
   constexpr int NDB = D / 32;
-  constexpr int HT = SPARSE ? 2 : 1;            // independent tile streams
-  constexpr int NW = 4 / HT;                    // waves of a group that load one tile
+  constexpr int NW = 4;                         // waves of a group that load one tile
   constexpr int LPW = C::TILE * 2 / 1024 / NW;  // 1 KB loads per wave per tile
-  __shared__ __align__(16) unsigned short kbuf_0[HT * C::TILE];
-  __shared__ __align__(16) unsigned short kbuf_1[HT * C::TILE];
-  __shared__ __align__(16) unsigned short kbuf_2[HT * C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_0[HT * C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_1[HT * C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_2[HT * C::TILE];
-  extern __shared__ __align__(16) unsigned short col_list[];  // SPARSE: two lists of mask columns
-  __shared__ int list_len[2];
+  __shared__ __align__(16) unsigned short kbuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_2[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_2[C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -288,61 +283,20 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   const BufRes dores = make_buf(a.dO + hoff, head_bytes);
 
   const int q_first = qt * BM;
-  const int hs = SPARSE ? (wg >> 1) : 0;  // this wave's tile stream
-  // block-sparse: the two mask rows this workgroup serves, one per stream
-  __shared__ int win_cnt[16];
-  const int2 mrows = SPARSE ? sparse_row_pair<CAUSAL>(a.mask, a.nb, nqt, qt, w, lane, win_cnt)
-                            : make_int2(2 * qt, 2 * qt + 1);
-  // query blocks interleave between the groups so that causal work is balanced; a
-  // block-sparse stream hs holds the 128 queries of its mask row
-  const int wave_q0 = SPARSE ? 128 * (hs == 0 ? mrows.x : mrows.y) + 32 * (2 * (wg & 1) + grp)
-                             : q_first + 32 * (2 * wg + grp);
+  // query blocks interleave between the groups so that causal work is balanced
+  const int wave_q0 = q_first + 32 * (2 * wg + grp);
   const int qrow = wave_q0 + l32;
-  const int wi = SPARSE ? (wg & 1) : wg;  // this wave's share of a tile load
-  unsigned short* const kb0 = kbuf_0 + hs * C::TILE;
-  unsigned short* const kb1 = kbuf_1 + hs * C::TILE;
-  unsigned short* const kb2 = kbuf_2 + hs * C::TILE;
-  unsigned short* const vb0 = vbuf_0 + hs * C::TILE;
-  unsigned short* const vb1 = vbuf_1 + hs * C::TILE;
-  unsigned short* const vb2 = vbuf_2 + hs * C::TILE;
-  int ntiles, nsteps;
-  if (SPARSE) {
-    constexpr int R = 128 / BN;  // key tiles per mask column
-    const int nb = a.nb;
-    if (w < 2) {  // wave h lists the columns kept by the mask row of stream h
-      const int r = w == 0 ? mrows.x : mrows.y;
-      const int ncol = r >= nb ? 0 : (CAUSAL ? r + 1 : nb);
-      const unsigned char* mrow = a.mask + (size_t)min(r, nb - 1) * nb;
-      int cnt = 0;
-      for (int base = 0; base < ncol; base += 64) {
-        const int col = base + lane;
-        const bool on = col < ncol && mrow[col] != 0;
-        const unsigned long long bal = __ballot(on);
-        if (on) col_list[w * nb + cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)col;
-        cnt += __popcll(bal);
-      }
-      if (lane == 0) list_len[w] = cnt;
-    }
-    __syncthreads();
-    auto tiles_of = [&](int h) __attribute__((always_inline)) -> int {
-      const int len = list_len[h];
-      int n = len * R;
-      if (len > 0 && col_list[h * nb + len - 1] == nb - 1) n -= R - ((N - (nb - 1) * 128 + BN - 1) / BN);
-      return n;
-    };
-    ntiles = tiles_of(hs);
-    nsteps = max(tiles_of(0), tiles_of(1));
-  } else {
-    const int kend = CAUSAL ? min(N, q_first + BM) : N;
-    ntiles = (kend + BN - 1) / BN;
-    nsteps = ntiles;
-  }
-  auto tile_at = [&](int t) __attribute__((always_inline)) -> int {
-    const int tt = min(t, ntiles - 1);
-    if (!SPARSE) return tt;
-    constexpr int R = 128 / BN;
-    return (int)col_list[hs * a.nb + tt / R] * R + tt % R;
-  };
+  const int wi = wg;  // this wave's share of a tile load
+  unsigned short* const kb0 = kbuf_0;
+  unsigned short* const kb1 = kbuf_1;
+  unsigned short* const kb2 = kbuf_2;
+  unsigned short* const vb0 = vbuf_0;
+  unsigned short* const vb1 = vbuf_1;
+  unsigned short* const vb2 = vbuf_2;
+  const int kend = CAUSAL ? min(N, q_first + BM) : N;
+  const int ntiles = (kend + BN - 1) / BN;
+  const int nsteps = ntiles;
+  auto tile_at = [&](int t) __attribute__((always_inline)) -> int { return min(t, ntiles - 1); };
   auto need_mask = [&](int kt) __attribute__((always_inline)) -> bool {
     const int k_first = kt * BN;
     return (k_first + BN > N) || (CAUSAL && k_first + BN - 1 > wave_q0);
@@ -351,7 +305,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   // Every tile buffer starts as zeros: K(-1) is read (times dS = 0) by the first
   // MFMA phase, and rows past N (which the range-checked loads may leave
   // unwritten) are multiplied by zeros, so they must hold finite values.
-  for (int i = tid; i < HT * C::TILE / 8; i += 512) {
+  for (int i = tid; i < C::TILE / 8; i += 512) {
     reinterpret_cast<uint4*>(kbuf_0)[i] = zero_uint4();
     reinterpret_cast<uint4*>(kbuf_1)[i] = zero_uint4();
     reinterpret_cast<uint4*>(kbuf_2)[i] = zero_uint4();
@@ -402,7 +356,6 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
 
   // Step t: buffers rotate with t mod 3.  kprev holds K(t-1), kcur K(t), vcur V(t);
   // group B fetches K(t+1) into knext, group A V(t+2) into vnext2.
-  // (a block-sparse stream that has run out of tiles only keeps the barriers)
   auto step = [&](int t, const unsigned short* kprev, const unsigned short* kcur, unsigned short* knext,
                   const unsigned short* vcur, unsigned short* vnext2) __attribute__((always_inline)) {
     const bool active = ntiles > 0 && t <= ntiles;
@@ -415,11 +368,9 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
       if (active) dma_k<D, BN, NW>(kres, knext, tile_at(t + 1), wi, lane);
       if (t >= 1 && t - 1 < ntiles) vector_phase(t - 1);
     }
-    // The mid-step barrier only keeps the two groups' phases in alternation: the ring
-    // buffers need just the end-of-step barrier (every buffer written in step t was last
-    // read in step t - 1).  Dense, the groups run faster left to drift; block-sparse,
-    // where the two tile streams differ in length, the barrier keeps them in step.
-    if (SPARSE) barrier_plain();
+    // No mid-step barrier: the ring buffers need just the end-of-step barrier (every
+    // buffer written in step t was last read in step t - 1), and the two groups run
+    // faster with their phases left to drift.
     if (grp == 0) {
       if (t < ntiles) vector_phase(t);
       wait_lgkm_vm<LPW>();  // V(t+1) has landed
@@ -450,7 +401,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
 // state: two at d = 128 (48 KB of LDS), three at d = 64, where 32-key tiles (24 KB)
 // let the kernel be held to 168 registers.
 // ---------------------------------------------------------------------------
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 1, 8)))
 void bwd_dq_short_kernel(BwdBf16Args a) {
   using C = TileCfg<D, BN>;
@@ -465,6 +416,8 @@ void bwd_dq_short_kernel(BwdBf16Args a) {
   __shared__ __align__(16) unsigned short vbuf_0[C::TILE];
   __shared__ __align__(16) unsigned short vbuf_1[C::TILE];
   __shared__ __align__(16) unsigned short vbuf_2[C::TILE];
+  extern __shared__ __align__(16) unsigned short col_list[];  // SPARSE: kept columns of the mask row
+  __shared__ int list_len;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -472,7 +425,7 @@ void bwd_dq_short_kernel(BwdBf16Args a) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int N = a.N;
-  const int nqt = (N + BM - 1) / BM;
+  const int nqt = (N + BM - 1) / BM;  // = the mask's row count: one workgroup per mask row
   const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / a.BH) : (int)(blockIdx.x / a.BH);  // longest rows first
   const int bh = (int)(blockIdx.x % a.BH);
   const size_t hoff = (size_t)bh * (size_t)N * D;
@@ -487,9 +440,39 @@ void bwd_dq_short_kernel(BwdBf16Args a) {
   const int wave_q0 = q_first + 32 * w;
   const int qrow = wave_q0 + l32;
   const int wi = __builtin_amdgcn_readfirstlane(w);  // this wave's share of a tile load
-  const int kend = CAUSAL ? min(N, q_first + BM) : N;
-  const int ntiles = (kend + BN - 1) / BN;
-  auto tile_at = [&](int t) __attribute__((always_inline)) -> int { return min(t, ntiles - 1); };
+  int ntiles;
+  if (SPARSE) {
+    // block-sparse: wave 0 lists the key columns its mask row keeps (128 keys each)
+    constexpr int R = 128 / BN;  // key tiles per mask column
+    const int nb = a.nb;
+    if (w == 0) {
+      const int ncol = CAUSAL ? qt + 1 : nb;
+      const unsigned char* mrow = a.mask + (size_t)qt * nb;
+      int cnt = 0;
+      for (int base = 0; base < ncol; base += 64) {
+        const int col = base + lane;
+        const bool on = col < ncol && mrow[col] != 0;
+        const unsigned long long bal = __ballot(on);
+        if (on) col_list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)col;
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) list_len = cnt;
+    }
+    __syncthreads();
+    // R tiles per listed column, minus those of the last column past N
+    const int len = list_len;
+    ntiles = len * R;
+    if (len > 0 && col_list[len - 1] == nb - 1) ntiles -= R - ((N - (nb - 1) * 128 + BN - 1) / BN);
+  } else {
+    const int kend = CAUSAL ? min(N, q_first + BM) : N;
+    ntiles = (kend + BN - 1) / BN;
+  }
+  auto tile_at = [&](int t) __attribute__((always_inline)) -> int {  // steps past the end repeat the last tile
+    const int tt = min(t, ntiles - 1);
+    if (!SPARSE) return tt;
+    constexpr int R = 128 / BN;
+    return (int)col_list[tt / R] * R + tt % R;
+  };
   auto need_mask = [&](int kt) __attribute__((always_inline)) -> bool {
     const int k_first = kt * BN;
     return (k_first + BN > N) || (CAUSAL && k_first + BN - 1 > wave_q0);
@@ -507,9 +490,11 @@ void bwd_dq_short_kernel(BwdBf16Args a) {
     reinterpret_cast<uint4*>(vbuf_2)[i] = zero_uint4();
   }
   barrier_lds();
-  dma_k<D, BN, 4>(kres, kbuf_0, tile_at(0), wi, lane);
-  dma_k<D, BN, 4>(vres, vbuf_0, tile_at(0), wi, lane);
-  dma_k<D, BN, 4>(vres, vbuf_1, tile_at(1), wi, lane);
+  if (ntiles > 0) {
+    dma_k<D, BN, 4>(kres, kbuf_0, tile_at(0), wi, lane);
+    dma_k<D, BN, 4>(vres, vbuf_0, tile_at(0), wi, lane);
+    dma_k<D, BN, 4>(vres, vbuf_1, tile_at(1), wi, lane);
+  }
   barrier_ring<LPW>();  // K(0) and V(0) have landed; V(1) may still be landing
 
   bf16x8 qf[D / 16], dof[D / 16];
@@ -546,7 +531,8 @@ void bwd_dq_short_kernel(BwdBf16Args a) {
     }
     barrier_ring<LPW>();
   };
-  for (int t = 0; t <= ntiles; t += 3) {
+  // a block-sparse row without any kept tile has dQ = 0 (its row statistics are stored)
+  for (int t = 0; ntiles > 0 && t <= ntiles; t += 3) {
     step(t, kbuf_2, kbuf_0, kbuf_1, vbuf_0, vbuf_2);
     if (t + 1 <= ntiles) step(t + 1, kbuf_0, kbuf_1, kbuf_2, vbuf_1, vbuf_0);
     if (t + 2 <= ntiles) step(t + 2, kbuf_1, kbuf_2, kbuf_0, vbuf_2, vbuf_1);
@@ -1118,6 +1104,26 @@ static void launch_prep_f32(const BwdParams& p, hipStream_t stream) {
 // faster, 12% on a grid of 128 workgroups), where without causal masking it lost 4%.
 constexpr int kShortCausalN = 2048;
 
+// dQ on 128-query workgroups (one per mask row when block-sparse)
+template <int D, bool CAUSAL, bool SPARSE>
+static void launch_dq_short(const BwdParams& p, const BwdBf16Args& a, hipStream_t stream) {
+  constexpr int SBN = 32;  // keys per tile: at d = 64, three workgroups per CU
+  const unsigned nqs = (unsigned)((p.N + 127) / 128);
+  const size_t dyn = SPARSE ? (((size_t)a.nb * 2 + 15) & ~(size_t)15) : 0;  // the column list
+  if (SPARSE)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_short_kernel<D, SBN, CAUSAL, SPARSE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  hipLaunchKernelGGL((bwd_dq_short_kernel<D, SBN, CAUSAL, SPARSE>), dim3(nqs * (unsigned)a.BH), dim3(256), dyn, stream,
+                     a);
+}
+
+// dQ on 256-query, 8-wave workgroups (d = 128, dense); 32-key tiles keep it within 256 VGPRs
+template <int D, bool CAUSAL>
+static void launch_dq_full(const BwdParams& p, const BwdBf16Args& a, hipStream_t stream) {
+  const unsigned nqb = (unsigned)((p.N + 255) / 256);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, 32, CAUSAL>), dim3(nqb * (unsigned)a.BH), dim3(512), 0, stream, a);
+}
+
 template <int D, bool CAUSAL, bool SPARSE>
 static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   BwdBf16Args a;
@@ -1141,16 +1147,11 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   a.neg = p.scale < 0.f ? 1 : 0;
   a.mask = p.mask;
   a.nb = (p.N + 127) / 128;
-  // block-sparse: the mask-row / mask-column lists live in dynamic LDS
+  // block-sparse: the dK/dV kernel's list of mask rows lives in dynamic LDS
   const size_t dyn_kv = SPARSE ? (((size_t)a.nb * 2 + 15) & ~(size_t)15) : 0;
-  const size_t dyn_q = SPARSE ? (((size_t)a.nb * 4 + 15) & ~(size_t)15) : 0;
-  constexpr int DQ_BN = D == 128 ? 32 : 64;  // keys per dQ tile (8 KB): keeps the d = 128 kernel within 256 VGPRs
-  if (SPARSE) {
+  if (SPARSE)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, SPARSE>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_kv);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_kernel<D, DQ_BN, CAUSAL, SPARSE>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_q);
-  }
   const unsigned nkb = (unsigned)a.nb;
   BwdBf16Args akv = a;
   if (a.group > 1) {  // per-query-head fp32 dK / dV, summed over the groups afterwards
@@ -1159,20 +1160,13 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
     akv.grad_bf16 = 0;
   }
   // the dQ kernel first: it also forms D and stores each row's (lse log2 e, -D) for the dK/dV kernel
-  bool short_dq = false;
-  if constexpr (!SPARSE && (CAUSAL || D == 64)) {
-    if (D == 64 || p.N <= kShortCausalN) {
-      short_dq = true;
-      const unsigned nqs = (unsigned)((p.N + 127) / 128);
-      constexpr int SBN = D == 64 ? 32 : DQ_BN;  // keys per tile: at d = 64, three workgroups per CU
-      hipLaunchKernelGGL((bwd_dq_short_kernel<D, SBN, CAUSAL>), dim3(nqs * (unsigned)a.BH), dim3(256), 0, stream,
-                         a);
-    }
-  }
-  if (!short_dq) {
-    const unsigned nqb = (unsigned)((p.N + 255) / 256);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, DQ_BN, CAUSAL, SPARSE>), dim3(nqb * (unsigned)a.BH), dim3(512), dyn_q,
-                       stream, a);
+  if constexpr (SPARSE || D == 64) {
+    launch_dq_short<D, CAUSAL, SPARSE>(p, a, stream);
+  } else if constexpr (CAUSAL) {
+    if (p.N <= kShortCausalN) launch_dq_short<D, CAUSAL, SPARSE>(p, a, stream);
+    else launch_dq_full<D, CAUSAL>(p, a, stream);
+  } else {
+    launch_dq_full<D, CAUSAL>(p, a, stream);
   }
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(nkb * (unsigned)a.BH), dim3(512), dyn_kv, stream,
                      akv);

@@ -22,11 +22,15 @@
 //   * O^T += V^T P^T on bf16 MFMA, V^T read with transposing LDS reads;
 //   * waves w and w+4 share a SIMD and alternate MFMA and softmax phases;
 //   * epilogue: O = acc / l, lse = m * |scale| + ln l (natural log).
-// Grouped-query heads read K/V head bh / group.  Block-sparse: each half of the
-// workgroup lists the key tiles kept by its 128-row mask row and visits only
-// those.  Short key ranges (causal N <= 2048, and at d = 64 causal N <= 8192 or
-// N <= 4096) go to fwd_bf16_short_kernel instead: 128 queries and 4 waves per
-// workgroup, two to four workgroups per CU, the same arithmetic.  fwd_f32_kernel is a plain fp32 kernel (one query per thread).
+// Grouped-query heads read K/V head bh / group.
+//
+// fwd_bf16_short_kernel: 128 queries and 4 waves per workgroup, two to four
+// workgroups per CU, the same tiles and arithmetic.  It serves short key ranges
+// (causal N <= 2048, and at d = 64 causal N <= 8192 or N <= 4096) and every
+// block-sparse forward: its 128 queries are one row of the 128 x 128 tile mask,
+// whose kept key tiles it lists and visits alone.
+//
+// fwd_f32_kernel is a plain fp32 kernel (one query per thread).
 #include <math.h>
 
 #include "fa_device.hpp"
@@ -224,32 +228,25 @@ __device__ __forceinline__ void store_output(const f32x16 (&oacc)[D / 32], float
 // issues MFMAs the other one's softmax runs on the vector ALU of the same SIMD.
 // The MFMA phase runs at raised wave priority so that its MFMAs issue first.
 // Tiles arrive by LDS-direct loads into a ring of three buffers, two steps
-// ahead of their use (group A fetches V, group B fetches K).
-// Block-sparse: the 256 queries span two 128-row mask rows, and SIMDs 0-1 serve
-// the first, SIMDs 2-3 the second.  Each half walks the key tiles of its own
-// mask row through its own half of every ring buffer (two waves per group load
-// a tile), so that neither pays for the other's tiles; both run the same number
-// of steps (the longer list) and the other half idles through the rest.
-template <int D, int BN, bool CAUSAL, bool SPARSE>
+// ahead of their use (group A fetches V, group B fetches K).  (Block-sparse
+// forwards run on fwd_bf16_short_kernel, whose 128 queries are one mask row.)
+template <int D, int BN, bool CAUSAL>
 __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   using C = FwdCfg<D, BN>;
   constexpr int BM = C::BM;
   constexpr int NSB = C::NSB;
   constexpr int NPT = C::NPT;
   constexpr int NDB = C::NDB;
-  constexpr int HT = SPARSE ? 2 : 1;                // independent tile streams
-  constexpr int NW = 4 / HT;                        // waves of a group that load one tile
-  constexpr int LPW = C::TILE * 2 / 1024 / NW;      // 1 KB loads per wave per tile
+  constexpr int NW = 4;                         // waves of a group that load one tile
+  constexpr int LPW = C::TILE * 2 / 1024 / NW;  // 1 KB loads per wave per tile
   // separate arrays (not one): the compiler then knows that LDS reads of one
   // buffer do not depend on LDS-direct loads still landing in another
-  __shared__ __align__(16) unsigned short kbuf_0[HT * C::TILE];
-  __shared__ __align__(16) unsigned short kbuf_1[HT * C::TILE];
-  __shared__ __align__(16) unsigned short kbuf_2[HT * C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_0[HT * C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_1[HT * C::TILE];
-  __shared__ __align__(16) unsigned short vbuf_2[HT * C::TILE];
-  extern __shared__ __align__(16) unsigned short col_list[];  // SPARSE: two lists of mask columns
-  __shared__ int list_len[2];
+  __shared__ __align__(16) unsigned short kbuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short kbuf_2[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_0[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_1[C::TILE];
+  __shared__ __align__(16) unsigned short vbuf_2[C::TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -278,65 +275,25 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   const BufRes ores = make_buf(a.o + hoff, head_bytes);
 
   const int q_first = qt * BM;
-  const int hs = SPARSE ? (wg >> 1) : 0;  // this wave's tile stream
-  // block-sparse: the two mask rows this workgroup serves, one per stream
-  __shared__ int win_cnt[16];
-  const int2 mrows = SPARSE ? sparse_row_pair<CAUSAL>(a.mask, a.nb, nqt, qt, w, lane, win_cnt)
-                            : make_int2(2 * qt, 2 * qt + 1);
-  // query blocks interleave between the groups so that causal work is balanced; a
-  // block-sparse stream hs holds the 128 queries of its mask row
-  const int wave_q0 = SPARSE ? 128 * (hs == 0 ? mrows.x : mrows.y) + 32 * (2 * (wg & 1) + grp)
-                             : q_first + 32 * (2 * wg + grp);
+  // query blocks interleave between the groups so that causal work is balanced
+  const int wave_q0 = q_first + 32 * (2 * wg + grp);
   const int qrow = wave_q0 + l32;
   // this wave's share of a tile load, made wave-uniform so that the loads' LDS
   // destinations (M0) are formed in scalar registers rather than read out of VGPRs
-  const int wi = __builtin_amdgcn_readfirstlane(SPARSE ? (wg & 1) : wg);
-  unsigned short* const kb0 = kbuf_0 + hs * C::TILE;
-  unsigned short* const kb1 = kbuf_1 + hs * C::TILE;
-  unsigned short* const kb2 = kbuf_2 + hs * C::TILE;
-  unsigned short* const vb0 = vbuf_0 + hs * C::TILE;
-  unsigned short* const vb1 = vbuf_1 + hs * C::TILE;
-  unsigned short* const vb2 = vbuf_2 + hs * C::TILE;
+  const int wi = __builtin_amdgcn_readfirstlane(wg);
+  unsigned short* const kb0 = kbuf_0;
+  unsigned short* const kb1 = kbuf_1;
+  unsigned short* const kb2 = kbuf_2;
+  unsigned short* const vb0 = vbuf_0;
+  unsigned short* const vb1 = vbuf_1;
+  unsigned short* const vb2 = vbuf_2;
 
-  // ---- which key tiles this wave's stream visits
-  int ntiles, nsteps;
-  if (SPARSE) {
-    constexpr int R = 128 / BN;  // key tiles per mask column
-    const int nb = a.nb;
-    if (w < 2) {  // wave h lists the columns kept by the mask row of stream h
-      const int r = w == 0 ? mrows.x : mrows.y;
-      const int ncol = r >= nb ? 0 : (CAUSAL ? r + 1 : nb);
-      const unsigned char* mrow = a.mask + (size_t)min(r, nb - 1) * nb;
-      int cnt = 0;
-      for (int base = 0; base < ncol; base += 64) {
-        const int col = base + lane;
-        const bool on = col < ncol && mrow[col] != 0;
-        const unsigned long long bal = __ballot(on);
-        if (on) col_list[w * nb + cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)col;
-        cnt += __popcll(bal);
-      }
-      if (lane == 0) list_len[w] = cnt;
-    }
-    __syncthreads();
-    // tiles of a stream: R per listed column, minus those of the last column past N
-    auto tiles_of = [&](int h) __attribute__((always_inline)) -> int {
-      const int len = list_len[h];
-      int n = len * R;
-      if (len > 0 && col_list[h * nb + len - 1] == nb - 1) n -= R - ((N - (nb - 1) * 128 + BN - 1) / BN);
-      return n;
-    };
-    ntiles = tiles_of(hs);
-    nsteps = max(tiles_of(0), tiles_of(1));
-  } else {
-    const int kend = CAUSAL ? min(N, q_first + BM) : N;
-    ntiles = (kend + BN - 1) / BN;
-    nsteps = ntiles;
-  }
+  // ---- the key tiles this workgroup visits
+  const int kend = CAUSAL ? min(N, q_first + BM) : N;
+  const int ntiles = (kend + BN - 1) / BN;
+  const int nsteps = ntiles;
   auto tile_at = [&](int t) __attribute__((always_inline)) -> int {  // steps past the end repeat the last tile
-    const int tt = min(t, ntiles - 1);
-    if (!SPARSE) return tt;
-    constexpr int R = 128 / BN;
-    return (int)col_list[hs * a.nb + tt / R] * R + tt % R;
+    return min(t, ntiles - 1);
   };
   auto need_mask = [&](int kt) __attribute__((always_inline)) -> bool {
     const int k_first = kt * BN;
@@ -364,7 +321,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   // V buffers start as zeros: the first MFMA phase multiplies buffer 2 by P = 0,
   // and key rows past N (which the range-checked loads may leave unwritten) must
   // hold finite values, since they are multiplied by P = 0 as well
-  for (int i = tid; i < HT * C::TILE / 8; i += 512) {
+  for (int i = tid; i < C::TILE / 8; i += 512) {
     reinterpret_cast<uint4*>(vbuf_0)[i] = zero_uint4();
     reinterpret_cast<uint4*>(vbuf_1)[i] = zero_uint4();
     reinterpret_cast<uint4*>(vbuf_2)[i] = zero_uint4();
@@ -409,7 +366,6 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
     // phase 2t: A fetches V(t+1) and runs G(t); B runs S(t-1).  Each group issues
     // its tile loads in its MFMA phase, where they cost nothing: issued next to
     // the vector work of a softmax phase they would slow it down.
-    // (a block-sparse stream that has run out of tiles only keeps the barriers)
     const bool active = ntiles > 0 && t <= ntiles;
     if (grp == 0) {
       if (active) {
@@ -431,8 +387,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
     }
     barrier_ring<LPW>();
   };
-  // Every wave runs the same steps (the barriers need it); a stream without any
-  // key tile (an empty block-sparse row) stays inactive: O = 0 and lse = -inf.
+  // every wave runs the same steps (the barriers need it)
   for (int t = 0; nsteps > 0 && t <= nsteps; t += 3) {
     step(t, kb0, kb2, vb2, vb1);
     if (t + 1 <= nsteps) step(t + 1, kb1, kb0, vb0, vb2);
@@ -456,7 +411,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
 // masking, outweigh the MFMA/softmax overlap of the 8-wave kernel.  With 64-key
 // tiles at d = 64 (32 KB of LDS) the kernel is held to 128 registers, so that four
 // workgroups share a CU; with 32-key tiles at d = 128 (32 KB) to 168, three per CU.
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && BN == 64 ? 4 : (D == 128 && BN == 32 ? 3 : 1), 8)))
 void fwd_bf16_short_kernel(FwdKernelArgs a) {
   using C = FwdCfg<D, BN>;
@@ -468,6 +423,8 @@ void fwd_bf16_short_kernel(FwdKernelArgs a) {
   __shared__ __align__(16) unsigned short kbuf_1[C::TILE];
   __shared__ __align__(16) unsigned short vbuf_0[C::TILE];
   __shared__ __align__(16) unsigned short vbuf_1[C::TILE];
+  extern __shared__ __align__(16) unsigned short col_list[];  // SPARSE: kept columns of the mask row
+  __shared__ int list_len;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -475,7 +432,7 @@ void fwd_bf16_short_kernel(FwdKernelArgs a) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int N = a.N;
-  const int nqt = (N + BM - 1) / BM;
+  const int nqt = (N + BM - 1) / BM;  // = the mask's row count: one workgroup per mask row
   int qt, bh;
   if (CAUSAL) {  // longest rows first
     qt = nqt - 1 - (int)(blockIdx.x / a.BH);
@@ -496,9 +453,39 @@ void fwd_bf16_short_kernel(FwdKernelArgs a) {
   const int wave_q0 = q_first + 32 * w;
   const int qrow = wave_q0 + l32;
   const int wi = __builtin_amdgcn_readfirstlane(w);  // this wave's share of a tile load
-  const int kend = CAUSAL ? min(N, q_first + BM) : N;
-  const int ntiles = (kend + BN - 1) / BN;
-  auto tile_at = [&](int t) __attribute__((always_inline)) -> int { return min(t, ntiles - 1); };
+  int ntiles;
+  if (SPARSE) {
+    // block-sparse: wave 0 lists the key columns its mask row keeps (128 keys each)
+    constexpr int R = 128 / BN;  // key tiles per mask column
+    const int nb = a.nb;
+    if (w == 0) {
+      const int ncol = CAUSAL ? qt + 1 : nb;
+      const unsigned char* mrow = a.mask + (size_t)qt * nb;
+      int cnt = 0;
+      for (int base = 0; base < ncol; base += 64) {
+        const int col = base + lane;
+        const bool on = col < ncol && mrow[col] != 0;
+        const unsigned long long bal = __ballot(on);
+        if (on) col_list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)col;
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) list_len = cnt;
+    }
+    __syncthreads();
+    // R tiles per listed column, minus those of the last column past N
+    const int len = list_len;
+    ntiles = len * R;
+    if (len > 0 && col_list[len - 1] == nb - 1) ntiles -= R - ((N - (nb - 1) * 128 + BN - 1) / BN);
+  } else {
+    const int kend = CAUSAL ? min(N, q_first + BM) : N;
+    ntiles = (kend + BN - 1) / BN;
+  }
+  auto tile_at = [&](int t) __attribute__((always_inline)) -> int {  // steps past the end repeat the last tile
+    const int tt = min(t, ntiles - 1);
+    if (!SPARSE) return tt;
+    constexpr int R = 128 / BN;
+    return (int)col_list[tt / R] * R + tt % R;
+  };
   auto need_mask = [&](int kt) __attribute__((always_inline)) -> bool {
     const int k_first = kt * BN;
     return (k_first + BN > N) || (CAUSAL && k_first + BN - 1 > wave_q0);
@@ -529,7 +516,7 @@ void fwd_bf16_short_kernel(FwdKernelArgs a) {
     reinterpret_cast<uint4*>(vbuf_1)[i] = zero_uint4();
   }
   barrier_lds();
-  dma_k<D, BN, 4>(kres, kbuf_0, tile_at(0), wi, lane);
+  if (ntiles > 0) dma_k<D, BN, 4>(kres, kbuf_0, tile_at(0), wi, lane);
   barrier_ring<0>();  // K(0) has landed
 
   // step t: buffers alternate with t mod 2 (kcur holds K(t), vprev V(t-1)); the
@@ -549,7 +536,8 @@ void fwd_bf16_short_kernel(FwdKernelArgs a) {
     }
     barrier_ring<0>();
   };
-  for (int t = 0; t <= ntiles; t += 2) {
+  // a block-sparse row without any kept tile stays inactive: O = 0 and lse = -inf
+  for (int t = 0; ntiles > 0 && t <= ntiles; t += 2) {
     step(t, kbuf_0, kbuf_1, vbuf_1, vbuf_0);
     if (t + 1 <= ntiles) step(t + 1, kbuf_1, kbuf_0, vbuf_0, vbuf_1);
   }
@@ -671,27 +659,25 @@ static FwdKernelArgs fwd_args(const FwdParams& p) {
   return a;
 }
 
-template <int D, int BN, bool CAUSAL, bool SPARSE>
+template <int D, int BN, bool CAUSAL>
 static hipError_t launch_fwd_bf16_t(const FwdParams& p, hipStream_t stream) {
   const FwdKernelArgs a = fwd_args(p);
   const int nqt = (p.N + 255) / 256;
-  const dim3 grid((unsigned)(nqt * a.BH));
-  size_t dyn = 0;
-  if (SPARSE) dyn = ((2 * (size_t)a.nb * sizeof(unsigned short)) + 15) & ~(size_t)15;
-  if (SPARSE && dyn > 0) {
-    // the tile list lives in dynamic LDS next to the static tiles
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel<D, BN, CAUSAL, SPARSE>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-  }
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, CAUSAL, SPARSE>), grid, dim3(512), dyn, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, CAUSAL>), dim3((unsigned)(nqt * a.BH)), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, int BN, bool CAUSAL>
+template <int D, int BN, bool CAUSAL, bool SPARSE = false>
 static hipError_t launch_fwd_short_t(const FwdParams& p, hipStream_t stream) {
   const FwdKernelArgs a = fwd_args(p);
   const int nqt = (p.N + 127) / 128;
-  hipLaunchKernelGGL((fwd_bf16_short_kernel<D, BN, CAUSAL>), dim3((unsigned)(nqt * a.BH)), dim3(256), 0, stream, a);
+  // block-sparse: the column list lives in dynamic LDS next to the static tiles
+  const size_t dyn = SPARSE ? (((size_t)a.nb * sizeof(unsigned short)) + 15) & ~(size_t)15 : 0;
+  if (SPARSE)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_short_kernel<D, BN, CAUSAL, SPARSE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  hipLaunchKernelGGL((fwd_bf16_short_kernel<D, BN, CAUSAL, SPARSE>), dim3((unsigned)(nqt * a.BH)), dim3(256), dyn,
+                     stream, a);
   return hipGetLastError();
 }
 
@@ -736,30 +722,22 @@ hipError_t launch_fwd(const FwdParams& p, hipStream_t stream) {
     if (p.d == 64) return p.causal ? launch_fwd_f32_t<64, true>(p, stream) : launch_fwd_f32_t<64, false>(p, stream);
     return p.causal ? launch_fwd_f32_t<128, true>(p, stream) : launch_fwd_f32_t<128, false>(p, stream);
   }
+  // block-sparse: one 128-query workgroup per mask row
+  if (sparse) {
+    if (p.d == 64)
+      return p.causal ? launch_fwd_short_t<64, 64, true, true>(p, stream) : launch_fwd_short_t<64, 64, false, true>(p, stream);
+    return p.causal ? launch_fwd_short_t<128, 32, true, true>(p, stream) : launch_fwd_short_t<128, 32, false, true>(p, stream);
+  }
   // short key ranges: 128-query, 4-wave workgroups, several per CU
-  if (!sparse) {
-    const long long nwg = (long long)((p.N + 127) / 128) * p.B * p.H;
-    if (p.d == 64) {
-      if (p.causal ? (p.N <= kShortD64CausalN && nwg >= kShortSmallTileGrid) : p.N <= kShortD64N)
-        return p.causal ? launch_fwd_short_t<64, 64, true>(p, stream) : launch_fwd_short_t<64, 64, false>(p, stream);
-      if (p.causal && p.N <= kShortCausalN) return launch_fwd_short_t<64, 128, true>(p, stream);
-    } else if (p.causal && p.N <= kShortCausalN) {
-      return launch_fwd_short_t<128, 32, true>(p, stream);
-    }
-  }
-  // block-sparse: 8 KB tiles (64 keys at d = 64, 32 at d = 128), two streams per workgroup
+  const long long nwg = (long long)((p.N + 127) / 128) * p.B * p.H;
   if (p.d == 64) {
-    if (sparse)
-      return p.causal ? launch_fwd_bf16_t<64, 64, true, true>(p, stream)
-                      : launch_fwd_bf16_t<64, 64, false, true>(p, stream);
-    return p.causal ? launch_fwd_bf16_t<64, 128, true, false>(p, stream)
-                    : launch_fwd_bf16_t<64, 128, false, false>(p, stream);
+    if (p.causal ? (p.N <= kShortD64CausalN && nwg >= kShortSmallTileGrid) : p.N <= kShortD64N)
+      return p.causal ? launch_fwd_short_t<64, 64, true>(p, stream) : launch_fwd_short_t<64, 64, false>(p, stream);
+    if (p.causal && p.N <= kShortCausalN) return launch_fwd_short_t<64, 128, true>(p, stream);
+    return p.causal ? launch_fwd_bf16_t<64, 128, true>(p, stream) : launch_fwd_bf16_t<64, 128, false>(p, stream);
   }
-  if (sparse)
-    return p.causal ? launch_fwd_bf16_t<128, 32, true, true>(p, stream)
-                    : launch_fwd_bf16_t<128, 32, false, true>(p, stream);
-  return p.causal ? launch_fwd_bf16_t<128, 64, true, false>(p, stream)
-                  : launch_fwd_bf16_t<128, 64, false, false>(p, stream);
+  if (p.causal && p.N <= kShortCausalN) return launch_fwd_short_t<128, 32, true>(p, stream);
+  return p.causal ? launch_fwd_bf16_t<128, 64, true>(p, stream) : launch_fwd_bf16_t<128, 64, false>(p, stream);
 }
 
 }  // namespace fa
