@@ -272,8 +272,10 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   const int l32 = lane & 31;
   const int N = a.N;
   const int nqt = (N + BM - 1) / BM;
-  const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / a.BH) : (int)(blockIdx.x / a.BH);  // longest rows first
-  const int bh = (int)(blockIdx.x % a.BH);
+  constexpr bool HR = !CAUSAL;  // head runs per XCD (grid_pos)
+  const GridPos gp = grid_pos<HR>(nqt, a.BH);
+  const int qt = CAUSAL ? nqt - 1 - gp.r : gp.r;  // longest rows first
+  const int bh = gp.bh;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const size_t kvoff = (size_t)(bh / a.group) * (size_t)N * D;  // grouped-query: shared K/V head
   const unsigned int head_bytes = (unsigned int)N * D * 2;
@@ -426,8 +428,10 @@ void bwd_dq_short_kernel(BwdBf16Args a) {
   const int l32 = lane & 31;
   const int N = a.N;
   const int nqt = (N + BM - 1) / BM;  // = the mask's row count: one workgroup per mask row
-  const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / a.BH) : (int)(blockIdx.x / a.BH);  // longest rows first
-  const int bh = (int)(blockIdx.x % a.BH);
+  constexpr bool HR = SPARSE || !CAUSAL;  // head runs per XCD (grid_pos)
+  const GridPos gp = grid_pos<HR>(nqt, a.BH);
+  const int qt = CAUSAL ? nqt - 1 - gp.r : gp.r;  // longest rows first
+  const int bh = gp.bh;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const size_t kvoff = (size_t)(bh / a.group) * (size_t)N * D;  // grouped-query: shared K/V head
   const unsigned int head_bytes = (unsigned int)N * D * 2;
@@ -623,8 +627,10 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int N = a.N;
-  const int kt = (int)(blockIdx.x / a.BH);  // causal: small kt = most query tiles, launched first
-  const int bh = (int)(blockIdx.x % a.BH);
+  constexpr bool HR = SPARSE || !CAUSAL;  // head runs per XCD (grid_pos)
+  const GridPos gp = grid_pos<HR>((N + C::BK - 1) / C::BK, a.BH);
+  const int kt = gp.r;  // causal: small kt = most query tiles, launched first
+  const int bh = gp.bh;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const unsigned int head_bytes = (unsigned int)N * D * 2;
   const BufRes qres = make_buf(a.q + hoff, head_bytes);

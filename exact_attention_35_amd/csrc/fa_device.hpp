@@ -101,6 +101,44 @@ __device__ __forceinline__ unsigned short bf16_lane_of(const uint4& u, int e) {
 
 __device__ __forceinline__ uint4 zero_uint4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// Consecutive workgroups of a launch go to the chip's eight XCDs in turn, and each
+// XCD has an L2 of its own.  xcd_run(i, G) renumbers workgroup i of G (a bijection on
+// [0, G)) so that the workgroups one XCD receives, in launch order, carry consecutive
+// numbers.
+__device__ __forceinline__ int xcd_run(int i, int G) {
+  constexpr int NX = 8;
+  const int per = (G + NX - 1) / NX;             // workgroups of the fuller XCDs
+  const int full = G % NX == 0 ? NX : G % NX;    // how many XCDs receive `per`
+  const int x = i % NX;
+  const int j = i / NX;
+  return x < full ? x * per + j : full * per + (x - full) * (per - 1) + j;
+}
+
+// Position of this workgroup in a grid of nrow * BH workgroups: its rank r in the
+// head's launch order and its head bh.  Either way each XCD serves B*H/8 heads when
+// B*H is a multiple of 8.  By default consecutive workgroups take consecutive heads
+// at one rank, so every XCD runs all ranks of a causal grid longest first.  With
+// HEAD_RUNS, B*H a multiple of 8 and more workgroups than the chip holds at once
+// (more than four per CU), each XCD works through its heads one after the other, so
+// the workgroups it runs at one time read the same head's tiles through its L2.  That
+// pays where rows are of like length or short against the whole launch (grids without
+// causal masking, block-sparse rows), and costs a tail in a dense causal grid, where
+// each head's longest rows would start late.
+struct GridPos {
+  int r;
+  int bh;
+};
+template <bool HEAD_RUNS>
+__device__ __forceinline__ GridPos grid_pos(int nrow, int BH) {
+  const int i = (int)blockIdx.x;
+  const int G = (int)gridDim.x;
+  if (HEAD_RUNS && (BH & 7) == 0 && G > 1024) {
+    const int L = xcd_run(i, G);
+    return {L % nrow, L / nrow};
+  }
+  return {i / BH, i % BH};
+}
+
 // ---- buffer (V#) memory access: the hardware range check returns zeros for
 // loads past `bytes` and drops stores past it, so tails need no branches.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

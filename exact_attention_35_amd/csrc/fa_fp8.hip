@@ -443,8 +443,10 @@ __global__ __launch_bounds__(512) void fwd_fp8_kernel(Fp8FwdArgs a) {
   const int l32 = lane & 31;
   const int N = a.N;
   const int nqt = (N + BM - 1) / BM;
-  const int qt = CAUSAL ? nqt - 1 - (int)(blockIdx.x / a.BH) : (int)(blockIdx.x / a.BH);
-  const int bh = (int)(blockIdx.x % a.BH);
+  constexpr bool HR = !CAUSAL;  // head runs per XCD (grid_pos)
+  const GridPos gp = grid_pos<HR>(nqt, a.BH);
+  const int qt = CAUSAL ? nqt - 1 - gp.r : gp.r;  // longest rows first
+  const int bh = gp.bh;
   const int kvh = bh / a.group;
   const unsigned int head_bytes = (unsigned int)N * D;
   const BufRes qres = make_buf(a.q + (size_t)bh * N * D, head_bytes);

@@ -258,14 +258,10 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   const int N = a.N;
   const int nqt = (N + BM - 1) / BM;
 
-  int qt, bh;
-  if (CAUSAL) {  // longest rows first
-    qt = nqt - 1 - (int)(blockIdx.x / a.BH);
-    bh = (int)(blockIdx.x % a.BH);
-  } else {
-    qt = (int)(blockIdx.x / a.BH);
-    bh = (int)(blockIdx.x % a.BH);
-  }
+  constexpr bool HR = !CAUSAL;  // head runs per XCD (grid_pos)
+  const GridPos gp = grid_pos<HR>(nqt, a.BH);
+  const int qt = CAUSAL ? nqt - 1 - gp.r : gp.r;  // longest rows first
+  const int bh = gp.bh;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const size_t kvoff = (size_t)(bh / a.group) * (size_t)N * D;  // grouped-query: shared K/V head
   const unsigned int head_bytes = (unsigned int)N * D * 2;
@@ -433,14 +429,10 @@ void fwd_bf16_short_kernel(FwdKernelArgs a) {
   const int l32 = lane & 31;
   const int N = a.N;
   const int nqt = (N + BM - 1) / BM;  // = the mask's row count: one workgroup per mask row
-  int qt, bh;
-  if (CAUSAL) {  // longest rows first
-    qt = nqt - 1 - (int)(blockIdx.x / a.BH);
-    bh = (int)(blockIdx.x % a.BH);
-  } else {
-    qt = (int)(blockIdx.x / a.BH);
-    bh = (int)(blockIdx.x % a.BH);
-  }
+  constexpr bool HR = SPARSE || !CAUSAL;  // head runs per XCD (grid_pos)
+  const GridPos gp = grid_pos<HR>(nqt, a.BH);
+  const int qt = CAUSAL ? nqt - 1 - gp.r : gp.r;  // longest rows first
+  const int bh = gp.bh;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const size_t kvoff = (size_t)(bh / a.group) * (size_t)N * D;  // grouped-query: shared K/V head
   const unsigned int head_bytes = (unsigned int)N * D * 2;
