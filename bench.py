@@ -345,13 +345,13 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel writing o, o_lo and lse (fa_fwd_ex)
-    "fwd": {"fetch_kib": 240136.6, "write_kib": 133320.5,
+    "fwd": {"fetch_kib": 247344.4, "write_kib": 133212.7,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "c1d6ed5f4fa1e168c1d3973d216f9aa88c2055dc65d1e6f92c4f87b4abcf68f5"},
+            "sha256": "5b4c5babfdee008227d8a56475978dd83d14ec74aba8b42ef2358729b79a9c18"},
     # bwd_dq_kernel (also reading o, o_lo for D) + bwd_dkdv_kernel (fa_bwd_ex)
-    "bwd": {"fetch_kib": 389008.9 + 363109.1, "write_kib": 133120.0 + 262144.0,
+    "bwd": {"fetch_kib": 391496.9 + 362767.6, "write_kib": 133120.0 + 262144.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "e706488eea988eab24b30fd35de4380915a578336375e3838de7df2c9eedf61b"},
+            "sha256": "66f87f5289058c508456b052d678ccc7822e49f1a9752c6f0d1d83a611249cc9"},
 }
 
 
