@@ -450,16 +450,7 @@ void bwd_dq_short_kernel(BwdBf16Args a) {
     constexpr int R = 128 / BN;  // key tiles per mask column
     const int nb = a.nb;
     if (w == 0) {
-      const int ncol = CAUSAL ? qt + 1 : nb;
-      const unsigned char* mrow = a.mask + (size_t)qt * nb;
-      int cnt = 0;
-      for (int base = 0; base < ncol; base += 64) {
-        const int col = base + lane;
-        const bool on = col < ncol && mrow[col] != 0;
-        const unsigned long long bal = __ballot(on);
-        if (on) col_list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)col;
-        cnt += __popcll(bal);
-      }
+      const int cnt = list_kept(a.mask + (size_t)qt * nb, 1, 0, CAUSAL ? qt + 1 : nb, col_list, lane);
       if (lane == 0) list_len = cnt;
     }
     __syncthreads();
@@ -591,17 +582,21 @@ __device__ __forceinline__ void sched_two_reads_per_mfma() {
   for (int i = 0; i < 3; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
-template <int D>
+template <int D, int KG>
 struct DkvCfg : TileCfg<D, 64> {
-  static constexpr int BK = 128;  // keys per workgroup
-  static constexpr int BQ = 64;   // queries per tile
+  static constexpr int BK = 32 * KG;                   // keys per workgroup
+  static constexpr int BQ = 64;                        // queries per tile
+  static constexpr int LPW = BQ * D * 2 / 1024 / KG;  // 1 KB loads per gradient wave and Q (or dO) tile
 };
 
-// Block-sparse (SPARSE): the workgroup's 128 keys are one mask column; it visits
-// the 64-query tiles of the mask rows that keep that column.
-template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
-  using C = DkvCfg<D>;
+// KG key groups of 32 keys, each served by a score wave and a gradient wave: KG = 4
+// (128 keys, 512 threads) puts the two waves of a group on one SIMD; KG = 2 (64 keys,
+// 256 threads, at d = 64 two workgroups per CU) puts every wave on a SIMD of its own.
+// Block-sparse (SPARSE): the workgroup's keys lie in one mask column; it visits the
+// 64-query tiles of the mask rows that keep that column.
+template <int D, bool CAUSAL, bool SPARSE, int KG>
+__global__ __launch_bounds__(128 * KG) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(BwdBf16Args a) {
+  using C = DkvCfg<D, KG>;
   constexpr int BQ = C::BQ;
   constexpr int NSB = C::NSB;  // 32-query blocks per tile
   constexpr int NPT = C::NPT;  // 16-query fragments per tile
@@ -615,15 +610,15 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
   __shared__ __align__(16) float2 st_0[BQ];
   __shared__ __align__(16) float2 st_1[BQ];
   __shared__ __align__(16) float2 st_2[BQ];
-  __shared__ __align__(16) uint4 xch[4][2 * NPT][64];  // per SIMD: P then dS fragments, per lane
+  __shared__ __align__(16) uint4 xch[KG][2 * NPT][64];  // per key group: P then dS fragments, per lane
   extern __shared__ __align__(16) unsigned short row_list[];  // SPARSE: mask rows that keep this column
   __shared__ int row_len;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: role branches are scalar
-  const int sw = w & 3;       // SIMD and key sub-block
-  const bool score = w < 4;   // role
+  const int sw = w % KG;      // key group (with KG = 4 also the SIMD)
+  const bool score = w < KG;  // role
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int N = a.N;
@@ -644,15 +639,9 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
   int T;  // query tiles this workgroup visits
   if (SPARSE) {
     const int nb = a.nb;
+    const int mcol = k0 >> 7;  // the mask column of this workgroup's keys
     if (w == 0) {
-      int cnt = 0;
-      for (int base = CAUSAL ? kt : 0; base < nb; base += 64) {
-        const int rb = base + lane;
-        const bool on = rb < nb && a.mask[(size_t)rb * nb + kt] != 0;
-        const unsigned long long bal = __ballot(on);
-        if (on) row_list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)rb;
-        cnt += __popcll(bal);
-      }
+      const int cnt = list_kept(a.mask + mcol, (size_t)nb, CAUSAL ? mcol : 0, nb, row_list, lane);
       if (lane == 0) row_len = cnt;
     }
     __syncthreads();
@@ -672,8 +661,8 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
   // tile i into buffer set i % 3, by the gradient waves
   auto fetch = [&](int i, unsigned short* qb, unsigned short* ob, float2* st) __attribute__((always_inline)) {
     const int tq = tile_q(i);
-    dma_k<D, BQ>(qres, qb, tq, sw, lane);
-    dma_k<D, BQ>(dores, ob, tq, sw, lane);
+    dma_k<D, BQ, KG>(qres, qb, tq, sw, lane);
+    dma_k<D, BQ, KG>(dores, ob, tq, sw, lane);
     if (sw == 0) {
       // the 64 rows' (lse log2 e, -D) pairs regrouped per four rows: LDS dword 8g + e holds
       // lse log2 e of row 4g + e for e < 4 and -D of row 4g + e - 4 for e >= 4, so that
@@ -688,11 +677,12 @@ __global__ __launch_bounds__(512) void bwd_dkdv_kernel(BwdBf16Args a) {
       }
     }
   };
-  constexpr int LOADS = 2 * C::KB_PER_WAVE + 2;  // loads of one fetch by gradient wave 0 (the others: two fewer)
+  constexpr int LOADS = 2 * C::LPW + 2;  // loads of one fetch by gradient wave 0 (the others: two fewer)
+  static_assert(LOADS < 16, "vmcnt field of the waits below");
 
   // Every buffer starts as zeros: rows past N (which the range-checked loads may
   // leave unwritten) are multiplied by P = dS = 0 and must hold finite values.
-  for (int i = tid; i < C::TILE / 8; i += 512) {
+  for (int i = tid; i < C::TILE / 8; i += 128 * KG) {
     reinterpret_cast<uint4*>(qbuf_0)[i] = zero_uint4();
     reinterpret_cast<uint4*>(qbuf_1)[i] = zero_uint4();
     reinterpret_cast<uint4*>(qbuf_2)[i] = zero_uint4();
@@ -1110,6 +1100,22 @@ static void launch_prep_f32(const BwdParams& p, hipStream_t stream) {
 // faster, 12% on a grid of 128 workgroups), where without causal masking it lost 4%.
 constexpr int kShortCausalN = 2048;
 
+constexpr int kDkvPairN = 2048;  // d = 64: 64-key dK/dV workgroups up to this N (twice it without causal masking)
+
+// dK/dV on workgroups of KG key groups (32 keys each)
+template <int D, bool CAUSAL, bool SPARSE, int KG>
+static void launch_dkdv(const BwdParams& p, const BwdBf16Args& a, hipStream_t stream) {
+  constexpr int BK = DkvCfg<D, KG>::BK;
+  const unsigned nkb = (unsigned)((p.N + BK - 1) / BK);
+  // block-sparse: the list of mask rows lives in dynamic LDS
+  const size_t dyn = SPARSE ? (((size_t)a.nb * 2 + 15) & ~(size_t)15) : 0;
+  if (SPARSE)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, SPARSE, KG>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE, KG>), dim3(nkb * (unsigned)a.BH), dim3(128 * KG), dyn,
+                     stream, a);
+}
+
 // dQ on 128-query workgroups (one per mask row when block-sparse)
 template <int D, bool CAUSAL, bool SPARSE>
 static void launch_dq_short(const BwdParams& p, const BwdBf16Args& a, hipStream_t stream) {
@@ -1153,12 +1159,6 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   a.neg = p.scale < 0.f ? 1 : 0;
   a.mask = p.mask;
   a.nb = (p.N + 127) / 128;
-  // block-sparse: the dK/dV kernel's list of mask rows lives in dynamic LDS
-  const size_t dyn_kv = SPARSE ? (((size_t)a.nb * 2 + 15) & ~(size_t)15) : 0;
-  if (SPARSE)
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL, SPARSE>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_kv);
-  const unsigned nkb = (unsigned)a.nb;
   BwdBf16Args akv = a;
   if (a.group > 1) {  // per-query-head fp32 dK / dV, summed over the groups afterwards
     akv.dk = p.part_k;
@@ -1174,8 +1174,14 @@ static void launch_bwd_bf16(const BwdParams& p, hipStream_t stream) {
   } else {
     launch_dq_full<D, CAUSAL>(p, a, stream);
   }
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, SPARSE>), dim3(nkb * (unsigned)a.BH), dim3(512), dyn_kv, stream,
-                     akv);
+  // dense d = 64 over short key ranges: 64-key workgroups, two per CU
+  if constexpr (D == 64 && !SPARSE) {
+    if (p.N <= (CAUSAL ? kDkvPairN : 2 * kDkvPairN)) {
+      launch_dkdv<D, CAUSAL, SPARSE, 2>(p, akv, stream);
+      return;
+    }
+  }
+  launch_dkdv<D, CAUSAL, SPARSE, 4>(p, akv, stream);
 }
 
 template <int D, bool CAUSAL>

@@ -451,16 +451,7 @@ void fwd_bf16_short_kernel(FwdKernelArgs a) {
     constexpr int R = 128 / BN;  // key tiles per mask column
     const int nb = a.nb;
     if (w == 0) {
-      const int ncol = CAUSAL ? qt + 1 : nb;
-      const unsigned char* mrow = a.mask + (size_t)qt * nb;
-      int cnt = 0;
-      for (int base = 0; base < ncol; base += 64) {
-        const int col = base + lane;
-        const bool on = col < ncol && mrow[col] != 0;
-        const unsigned long long bal = __ballot(on);
-        if (on) col_list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)col;
-        cnt += __popcll(bal);
-      }
+      const int cnt = list_kept(a.mask + (size_t)qt * nb, 1, 0, CAUSAL ? qt + 1 : nb, col_list, lane);
       if (lane == 0) list_len = cnt;
     }
     __syncthreads();

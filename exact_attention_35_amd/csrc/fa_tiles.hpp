@@ -81,6 +81,33 @@ __device__ __forceinline__ void dma_v(BufRes vres, unsigned short* vbuf, int kt,
   }
 }
 
+// Block-sparse schedules: one wave lists, in ascending order, the indices i in
+// [first, end) whose mask flag flags[i * stride] is nonzero, into list[] in LDS, and
+// returns their count (wave-uniform).  The flags of 512 indices are requested before
+// any of them is examined, so the scan waits for one round of loads per 512 indices
+// instead of one per 64.
+__device__ __forceinline__ int list_kept(const unsigned char* flags, size_t stride, int first, int end,
+                                         unsigned short* list, int lane) {
+  int cnt = 0;
+  for (int base = first; base < end; base += 512) {
+    unsigned char f[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {  // unconditional loads (indices past the end re-read the last flag)
+      const int i = min(base + 64 * u + lane, end - 1);
+      f[u] = flags[(size_t)i * stride];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = base + 64 * u + lane;
+      const bool on = i < end && f[u] != 0;
+      const unsigned long long bal = __ballot(on);
+      if (on) list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = (unsigned short)i;
+      cnt += __popcll(bal);
+    }
+  }
+  return cnt;
+}
+
 // wait for this wave's LDS-direct loads (they count as vector-memory loads)
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
