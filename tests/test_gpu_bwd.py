@@ -152,8 +152,9 @@ def test_edge_lengths_bf16(d, causal):
 def test_causal_around_short_sequence_limit(d):
     """At d = 128 the dQ of causal sequences of up to 2048 keys runs on the 128-query, 4-wave
     kernel and of longer ones on the 256-query, 8-wave kernel (at d = 64 the 4-wave kernel
-    serves both): both sides of that limit, ragged, with the forward's low-order part of O
-    (as the benchmark runs it) and bf16 gradients."""
+    serves both, while the dK/dV of causal d = 64 sequences of up to 2048 keys runs on 64-key
+    workgroups and of longer ones on 128-key workgroups): both sides of those limits, ragged,
+    with the forward's low-order part of O (as the benchmark runs it) and bf16 gradients."""
     scale = api.default_scale(d)
     for n in (2047, 2049):
         announce(f"bwd bf16 causal N={n} d={d}")
@@ -174,7 +175,9 @@ def test_causal_around_short_sequence_limit(d):
 @pytest.mark.parametrize("n, causal", [(4100, True), (3000, False)])
 def test_d64_backward_longer_sequences(n, causal):
     """At d = 64 the 128-query, 4-wave dQ kernel serves every length, with and without causal
-    masking: two ragged lengths past 2048 against the oracle (fp32 gradients)."""
+    masking: two ragged lengths past 2048 against the oracle (fp32 gradients).  N = 3000
+    without causal masking runs the dK/dV on 64-key workgroups (up to 4096 keys), N = 4100
+    causal on 128-key workgroups."""
     announce(f"bwd bf16 N={n} d=64 causal={causal}")
     q, k, v, do = inputs.random_case(47, 1, 2, n, 64, "bf16", backward=True)
     scale = api.default_scale(64)
