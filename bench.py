@@ -345,13 +345,13 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel writing o, o_lo and lse (fa_fwd_ex)
-    "fwd": {"fetch_kib": 247344.4, "write_kib": 133212.7,
+    "fwd": {"fetch_kib": 249355.0, "write_kib": 133173.2,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "5b4c5babfdee008227d8a56475978dd83d14ec74aba8b42ef2358729b79a9c18"},
+            "sha256": "16250a5ad2609e998e0bcd5acd529270b37fe591359e0420b6f8221c27e370bd"},
     # bwd_dq_kernel (also reading o, o_lo for D) + bwd_dkdv_kernel (fa_bwd_ex)
-    "bwd": {"fetch_kib": 391496.9 + 362767.6, "write_kib": 133120.0 + 262144.0,
+    "bwd": {"fetch_kib": 392638.4 + 363066.9, "write_kib": 133120.0 + 262144.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "66f87f5289058c508456b052d678ccc7822e49f1a9752c6f0d1d83a611249cc9"},
+            "sha256": "384efe21b483049b7575d1439d5a21b616b3bd8a3a0bf6b2ed9d2af6dca67ca0"},
 }
 
 
