@@ -145,13 +145,20 @@ def kernel_table():
             tm = torch.from_numpy(mask).to("cuda:0")
             ms = time_calls(lambda: api.forward_blocksparse(tq, tk, tv, tm, w.scale, w.causal), 10)
             entry.update(fwd_ms=ms, fwd_tflops=flops_fwd(w, dens) / ms / 1e9, density=dens)
+            ts = time_launches(lambda: api.forward_blocksparse(tq, tk, tv, tm, w.scale, w.causal), 10)
+            entry.update(fwd_median_ms=ts[len(ts) // 2], fwd_min_ms=ts[0],
+                         fwd_median_frac_peak=flops_fwd(w, dens) / ts[len(ts) // 2] / 1e9 / PEAK_BF16_TFLOPS)
             # block-sparse backward on the same mask (D formed from o + o_lo, as in training)
             o, lse, o_lo = api.forward_train(tq, tk, tv, w.scale, w.causal, block_mask=tm)
             tdo = to_dev(inputs.draw(w.index, inputs.SLOT_DO, w.shape), torch.bfloat16)
             ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d), dtype=torch.uint8, device="cuda:0")
-            bms = time_calls(lambda: api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws,
-                                                  block_mask=tm, o_lo=o_lo), 5)
+            bfn = lambda: api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws,  # noqa: E731
+                                       block_mask=tm, o_lo=o_lo)
+            bms = time_calls(bfn, 5)
             entry.update(bwd_ms=bms, bwd_tflops=2.5 * flops_fwd(w, dens) / bms / 1e9)
+            bts = time_launches(bfn, 5)
+            entry.update(bwd_median_ms=bts[len(bts) // 2], bwd_min_ms=bts[0],
+                         bwd_median_frac_peak=2.5 * flops_fwd(w, dens) / bts[len(bts) // 2] / 1e9 / PEAK_BF16_TFLOPS)
             del o, lse, o_lo, tdo, ws
         else:
             ms = time_calls(lambda: api.forward(tq, tk, tv, w.scale, w.causal), 20)
@@ -187,9 +194,12 @@ def kernel_table():
                 tdo = to_dev(inputs.draw(w.index, inputs.SLOT_DO, w.shape), torch.bfloat16)
                 ws = torch.empty(api.bwd_workspace_size(w.B, w.H, w.N, w.d, H_kv=w.kv_heads), dtype=torch.uint8,
                                  device="cuda:0")
-                bms = time_calls(lambda: api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws,
-                                                      o_lo=o_lo), 10)
+                bfn = lambda: api.backward(tq, tk, tv, o, lse, tdo, w.scale, w.causal, workspace=ws,  # noqa: E731
+                                           o_lo=o_lo)
+                bms = time_calls(bfn, 10)
                 entry.update(bwd_ms=bms, bwd_tflops=2.5 * flops_fwd(w) / bms / 1e9)
+                bts = time_launches(bfn, 10)
+                entry.update(bwd_median_ms=bts[len(bts) // 2], bwd_min_ms=bts[0])
         entry["fwd_frac_peak"] = entry["fwd_tflops"] / PEAK_BF16_TFLOPS
         rows[name] = {k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in entry.items()}
         del tq, tk, tv
