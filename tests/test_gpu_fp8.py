@@ -245,3 +245,41 @@ def test_fp8_score_accumulation_property(d):
     report(f"fp8 score accumulation d={d}", err_over_maxprod_log2=float(np.log2(max(ratio, 2.0 ** -40))),
            err_over_gate=float((err / (gate_term + fp32_slack)).max()))
     assert np.all(err <= gate_term + fp32_slack), float((err / (gate_term + fp32_slack)).max())
+
+
+def test_forward_fp8_head_runs():
+    """Without causal masking the FP8 forward's grid runs head by head on each XCD once B*H is
+    a multiple of 8 and the grid has more than 1024 workgroups: B=8, H=8, N=4500, d=128 (1152
+    workgroups of 256 queries).  Outputs start as NaN, so every (block, head) pair must be
+    written; heads at the start, middle and end of the grid, on 128 sampled rows each, within
+    the bound."""
+    from exact_attention_35_amd import _lib
+
+    B, H, N, d = 8, 8, 4500, 128
+    name = f"fp8 fwd head runs B={B} H={H} N={N} d={d}"
+    announce(name)
+    q8, k8, v8, _ = _fwd_case(77, B, H, H, N, d)
+    (qc, qs), (kc, ks), (vc, vs) = q8, k8, v8
+    scale = api.default_scale(d)
+    o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device=DEV)
+    tq, tqs, tk, tks, tv, tvs = _u8(qc), _f32(qs), _u8(kc), _f32(ks), _u8(vc), _f32(vs)
+    st = _lib.load().fa_fwd_fp8(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), tqs.data_ptr(), tks.data_ptr(),
+                                tvs.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H, N, d, scale, 0,
+                                torch.cuda.current_stream().cuda_stream)
+    _lib.check(st, "fa_fwd_fp8")
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all()), "entries no workgroup wrote"
+    rows = inputs.sample_rows(N, 128, 77)
+    go_all, gl_all = host(o), host(lse)
+    for b, h in ((0, 0), (3, 6), (7, 7)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        dq, dk, dv = of8.dequantize(qc[sl], qs[sl]), of8.dequantize(kc[sl], ks[sl]), of8.dequantize(vc[sl], vs[sl])
+        ro, rl = oracle.forward_rows(dq, dk, dv, rows, scale, False)
+        gate, lgate = _gates(dq, dk, dv, ro, scale, False, rows)
+        err = np.abs(go_all[sl][:, :, rows] - ro)
+        lerr = np.abs(gl_all[sl][:, :, rows] - rl)
+        report(f"{name} head ({b}, {h})", o=float(err.max()), o_over_gate=float((err / gate).max()),
+               lse=float(lerr.max()), lse_over_gate=float((lerr / lgate).max()))
+        assert np.all(err <= gate), (b, h, float((err / gate).max()))
+        assert np.all(lerr <= lgate), (b, h, float((lerr / lgate).max()))
