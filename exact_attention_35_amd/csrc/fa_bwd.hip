@@ -273,7 +273,7 @@ __global__ __launch_bounds__(512) void bwd_dq_kernel(BwdBf16Args a) {
   const int N = a.N;
   const int nqt = (N + BM - 1) / BM;
   constexpr bool HR = !CAUSAL;  // head runs per XCD (grid_pos)
-  const GridPos gp = CAUSAL ? grid_pos_causal(nqt, a.BH, 32, N) : grid_pos<HR>(nqt, a.BH);
+  const GridPos gp = CAUSAL ? grid_pos_causal(nqt, a.BH, 32) : grid_pos<HR>(nqt, a.BH);
   const int qt = CAUSAL ? nqt - 1 - gp.r : gp.r;  // longest rows first
   const int bh = gp.bh;
   const size_t hoff = (size_t)bh * (size_t)N * D;
@@ -429,7 +429,7 @@ void bwd_dq_short_kernel(BwdBf16Args a) {
   const int N = a.N;
   const int nqt = (N + BM - 1) / BM;  // = the mask's row count: one workgroup per mask row
   constexpr bool HR = SPARSE || !CAUSAL;  // head runs per XCD (grid_pos)
-  const GridPos gp = (CAUSAL && !SPARSE) ? grid_pos_causal(nqt, a.BH, 32 * (D == 64 ? 3 : 2), N)
+  const GridPos gp = (CAUSAL && !SPARSE) ? grid_pos_causal(nqt, a.BH, 32 * (D == 64 ? 3 : 2))
                                          : grid_pos<HR>(nqt, a.BH);
   const int qt = CAUSAL ? nqt - 1 - gp.r : gp.r;  // longest rows first
   const int bh = gp.bh;
@@ -624,7 +624,7 @@ __global__ __launch_bounds__(128 * KG) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int l32 = lane & 31;
   const int N = a.N;
   constexpr bool HR = SPARSE || !CAUSAL;  // head runs per XCD (grid_pos)
-  const GridPos gp = (CAUSAL && !SPARSE) ? grid_pos_causal((N + C::BK - 1) / C::BK, a.BH, 32 * (4 / KG), N)
+  const GridPos gp = (CAUSAL && !SPARSE) ? grid_pos_causal((N + C::BK - 1) / C::BK, a.BH, 32 * (4 / KG))
                                          : grid_pos<HR>((N + C::BK - 1) / C::BK, a.BH);
   const int kt = gp.r;  // causal: small kt = most query tiles, launched first
   const int bh = gp.bh;

@@ -133,15 +133,14 @@ struct GridPos {
 // work (about g nrow^2 / 2 row steps over `slots` resident workgroups) outlasts its
 // longest row (nrow steps): the XCD's resident workgroups then read the K/V of g heads
 // through its L2 instead of those of all its heads, without starting any long row late.
-// Used up to N = 4096, where a few heads' K/V are within reach of the L2 (at 16K one
-// head's K/V alone is 8 MB at d = 128, and grouping measured 0.6% slower); otherwise,
-// and when it would leave a single group, the order is the default one of grid_pos.
-__device__ __forceinline__ GridPos grid_pos_causal(int nrow, int BH, int slots, int N) {
+// When it would leave a single group (or B*H is not a multiple of 8) the order is the
+// default one of grid_pos.
+__device__ __forceinline__ GridPos grid_pos_causal(int nrow, int BH, int slots) {
   const int i = (int)blockIdx.x;
   const int hx = BH >> 3;  // heads per XCD
   int g = 2;
   while (g < hx && g * nrow < 2 * slots) g <<= 1;
-  if ((BH & 7) != 0 || g >= hx || hx % g != 0 || N > 4096) return {i / BH, i % BH};
+  if ((BH & 7) != 0 || g >= hx || hx % g != 0) return {i / BH, i % BH};
   const int G = (int)gridDim.x;
   const int L = xcd_run(i, G);
   const int per = G >> 3;

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(512) void fwd_bf16_kernel(FwdKernelArgs a) {
   const int nqt = (N + BM - 1) / BM;
 
   constexpr bool HR = !CAUSAL;  // head runs per XCD (grid_pos)
-  const GridPos gp = CAUSAL ? grid_pos_causal(nqt, a.BH, 32, N) : grid_pos<HR>(nqt, a.BH);
+  const GridPos gp = CAUSAL ? grid_pos_causal(nqt, a.BH, 32) : grid_pos<HR>(nqt, a.BH);
   const int qt = CAUSAL ? nqt - 1 - gp.r : gp.r;  // longest rows first
   const int bh = gp.bh;
   const size_t hoff = (size_t)bh * (size_t)N * D;
@@ -430,7 +430,7 @@ void fwd_bf16_short_kernel(FwdKernelArgs a) {
   const int N = a.N;
   const int nqt = (N + BM - 1) / BM;  // = the mask's row count: one workgroup per mask row
   constexpr bool HR = SPARSE || !CAUSAL;  // head runs per XCD (grid_pos)
-  const GridPos gp = (CAUSAL && !SPARSE) ? grid_pos_causal(nqt, a.BH, 32 * (D == 64 && BN == 64 ? 4 : (D == 128 && BN == 32 ? 3 : 2)), N)
+  const GridPos gp = (CAUSAL && !SPARSE) ? grid_pos_causal(nqt, a.BH, 32 * (D == 64 && BN == 64 ? 4 : (D == 128 && BN == 32 ? 3 : 2)))
                                          : grid_pos<HR>(nqt, a.BH);
   const int qt = CAUSAL ? nqt - 1 - gp.r : gp.r;  // longest rows first
   const int bh = gp.bh;
