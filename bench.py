@@ -355,13 +355,13 @@ TRAFFIC_FETCH_SCALE = 2.0
 TRAFFIC_WRITE_SCALE = 1.0
 MEASURED_TRAFFIC = {
     # fwd_bf16_kernel writing o, o_lo and lse (fa_fwd_ex)
-    "fwd": {"fetch_kib": 249355.0, "write_kib": 133173.2,
+    "fwd": {"fetch_kib": 247409.1, "write_kib": 133150.1,
             "sources": ["fa_fwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "16250a5ad2609e998e0bcd5acd529270b37fe591359e0420b6f8221c27e370bd"},
+            "sha256": "285cca64868389f10df88a08b658ece7a4b8c8d79deddfab7ef370505cc3f434"},
     # bwd_dq_kernel (also reading o, o_lo for D) + bwd_dkdv_kernel (fa_bwd_ex)
-    "bwd": {"fetch_kib": 392638.4 + 363066.9, "write_kib": 133120.0 + 262144.0,
+    "bwd": {"fetch_kib": 389220.5 + 363384.7, "write_kib": 133120.0 + 262144.0,
             "sources": ["fa_bwd.hip", "fa_device.hpp", "fa_tiles.hpp"],
-            "sha256": "384efe21b483049b7575d1439d5a21b616b3bd8a3a0bf6b2ed9d2af6dca67ca0"},
+            "sha256": "d26a4711fd58490c537e25e32f13b5cb77aa70b2c58ffe0d056d1939bbecb7d4"},
 }
 
 
